@@ -1,0 +1,42 @@
+"""CPU fp64 oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or run anything in this package.  The product path
+(the HIP library and its Python binding) never calls it, and the two share
+no code: no kernels, headers, helpers, tables or pre/post-processing.
+
+Contents
+  dense.attention         full-matrix softmax attention, fp64 (the definition)
+  dense.softmax_probs     the normalised probability matrix P of one slice
+  dense.attention_rows    the same definition evaluated one output row at a time
+  dense.split_partials    per-chunk partial results of split-KV decoding
+  dense.merge_partials    the log-sum-exp merge of those partials
+  dense.decode_splitkv    split-KV decoding = merge(split(...))
+  brute.attention_brute   pure-Python scalar loops, for tiny inputs only
+
+Every function is pinned by tests in ``tests/test_oracle.py`` against
+closed forms, hand-derived worked examples (``tests/golden/``), invariants of
+the definition, brute force and ``torch.nn.functional.scaled_dot_product_attention``
+in fp64 on the CPU.  No function here is "parity unpinned".
+"""
+from .dense import (
+    attention,
+    attention_rows,
+    decode_splitkv,
+    merge_partials,
+    softmax_probs,
+    split_partials,
+    split_bounds,
+)
+from .brute import attention_brute
+
+__all__ = [
+    "attention",
+    "attention_rows",
+    "decode_splitkv",
+    "merge_partials",
+    "softmax_probs",
+    "split_partials",
+    "split_bounds",
+    "attention_brute",
+]

@@ -1,0 +1,87 @@
+"""Seeded synthetic workloads for exact attention: shapes and input generators.
+
+This module holds the workload table and the random-input recipe shared by the
+CPU oracle's tests, the GPU parity tests, smoke() and bench.py.  It contains
+none of the attention arithmetic: it only draws numbers.
+
+Recipe (the same everywhere):
+  * numpy ``Generator(PCG64(seed))``;
+  * Q, then K, then V are drawn with ``standard_normal(dtype=float32)`` in C
+    order over their full ``[B, H, S, D]`` shape, one leading-batch slice at a
+    time (the draw stream is the same as one whole-array draw);
+  * each value is rounded to IEEE fp16 (round-to-nearest-even).
+The causal and non-causal runs of one workload reuse the same tensors.
+
+The shapes follow the pages' workloads: the LLaMA-7B prefill shape
+(1, 32, 4096, 4096, 128) and the 8K-context single-query decode shape of the
+"FlashAttention-2 MMA" benchmark tables, the B8/H16/S256/D64 shape of
+"Flash Attention 101"'s A100 benchmark, and a D=256 large-head prefill.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: tuple  # the mask settings this workload is run with
+    seed: int
+    kind: str  # "prefill" or "decode"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def shape_q(self):
+        return (self.B, self.H, self.Sq, self.D)
+
+    def shape_kv(self):
+        return (self.B, self.H, self.Sk, self.D)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 128, 64, (False, True), 1, "prefill"),
+    "small": Workload("small", 8, 16, 256, 256, 64, (False, True), 2, "prefill"),
+    "llama7b_prefill": Workload("llama7b_prefill", 1, 32, 4096, 4096, 128, (True,), 3, "prefill"),
+    "decode_8k": Workload("decode_8k", 16, 32, 1, 8192, 128, (False,), 4, "decode"),
+    "d256_prefill": Workload("d256_prefill", 1, 16, 2048, 2048, 256, (True,), 5, "prefill"),
+}
+
+
+def _draw_fp16(gen: np.random.Generator, shape) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float16)
+    for b in range(shape[0]):
+        out[b] = gen.standard_normal(shape[1:], dtype=np.float32).astype(np.float16)
+    return out
+
+
+def make_qkv(B: int, H: int, Sq: int, Sk: int, D: int, seed: int):
+    """Q [B,H,Sq,D], K and V [B,H,Sk,D] as fp16 numpy arrays, N(0,1) draws."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    q = _draw_fp16(gen, (B, H, Sq, D))
+    k = _draw_fp16(gen, (B, H, Sk, D))
+    v = _draw_fp16(gen, (B, H, Sk, D))
+    return q, k, v
+
+
+def workload_inputs(w: Workload):
+    return make_qkv(w.B, w.H, w.Sq, w.Sk, w.D, w.seed)
+
+
+def sample_rows(w: Workload, count: int, seed: int = 12345):
+    """A seeded sample of (b, h, i) output rows, always including the first
+    and last row of the first and last (b, h) slice."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    picks = {(0, 0, 0), (w.B - 1, w.H - 1, w.Sq - 1), (0, 0, w.Sq - 1), (w.B - 1, w.H - 1, 0)}
+    while len(picks) < count + 4:
+        picks.add((int(gen.integers(w.B)), int(gen.integers(w.H)), int(gen.integers(w.Sq))))
+    return sorted(picks)
