@@ -1,0 +1,139 @@
+"""MI355X (gfx950) exact-attention forward: Python binding of libfa_hip.so.
+
+The functions below carry the C-ABI names of include/fa.h and only marshal
+arguments: torch tensors supply device memory and the current HIP stream,
+the HIP kernels do all of the work.  There is no fallback path: if the
+library is missing or the tensors are not on a GPU, the call raises.
+
+    o, lse = fa_fwd(q, k, v, causal=True)                  # q,k,v fp16 [B,H,S,D]
+    o, lse = fa_decode_splitkv(q, k, v, num_splits=0)      # Sq == 1, 0 = auto
+"""
+from __future__ import annotations
+
+import math
+
+from . import _capi
+from ._capi import FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FAError, LIB_PATH
+
+__all__ = [
+    "fa_fwd",
+    "fa_decode_splitkv",
+    "fa_decode_splitkv_ws",
+    "fa_decode_workspace_bytes",
+    "fa_decode_auto_splits",
+    "fa_status_string",
+    "fa_last_error",
+    "FAError",
+    "LIB_PATH",
+    "FA_OK",
+    "FA_ERR_INVALID_ARG",
+    "FA_ERR_UNSUPPORTED",
+    "FA_ERR_HIP",
+]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _check_qkv(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16 (got {t.dtype})")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, S, D] tensor")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return B, H, Sq, k.shape[2], D
+
+
+def _outputs(q, o, lse):
+    torch = _torch()
+    B, H, Sq, D = q.shape
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if o.dtype != torch.float16 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous fp16 tensor shaped like q on its device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [B, H, Sq] tensor on q's device")
+    return o, lse
+
+
+def _stream(q, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None):
+    """Exact attention forward; returns (o, lse).  See fa_fwd in include/fa.h."""
+    B, H, Sq, Sk, D = _check_qkv(q, k, v)
+    o, lse = _outputs(q, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _capi.load()
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream))
+    _capi.check(st, "fa_fwd")
+    return o, lse
+
+
+def fa_decode_splitkv(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None, num_splits=0):
+    """Split-KV single-query decoding; returns (o, lse).  num_splits <= 0 = auto."""
+    B, H, Sq, Sk, D = _check_qkv(q, k, v)
+    o, lse = _outputs(q, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _capi.load()
+    st = lib.fa_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream),
+                               int(num_splits))
+    _capi.check(st, "fa_decode_splitkv")
+    return o, lse
+
+
+def fa_decode_splitkv_ws(q, k, v, workspace, o=None, lse=None, causal=False, scale=None, stream=None,
+                         num_splits=0):
+    """fa_decode_splitkv with a caller-owned workspace tensor (any dtype, contiguous)."""
+    B, H, Sq, Sk, D = _check_qkv(q, k, v)
+    o, lse = _outputs(q, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be contiguous and on q's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = _capi.load()
+    st = lib.fa_decode_splitkv_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream),
+                                  int(num_splits), workspace.data_ptr(), nbytes)
+    _capi.check(st, "fa_decode_splitkv_ws")
+    return o, lse
+
+
+def fa_decode_workspace_bytes(B, H, D, num_splits):
+    return int(_capi.load().fa_decode_workspace_bytes(B, H, D, num_splits))
+
+
+def fa_decode_auto_splits(B, H, Sk, num_cus):
+    return int(_capi.load().fa_decode_auto_splits(B, H, Sk, num_cus))
+
+
+def fa_status_string(status):
+    return _capi.status_name(status)
+
+
+def fa_last_error():
+    return _capi.last_error()

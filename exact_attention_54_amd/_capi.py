@@ -1,0 +1,72 @@
+"""ctypes view of the C ABI in include/fa.h (libfa_hip.so, built in-tree).
+
+Argument marshalling only: every step of the attention path runs in the
+HIP library.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libfa_hip.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+# name -> (restype, argtypes); mirrors include/fa.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+_COMMON = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]
+SIGNATURES = {
+    "fa_fwd": (_I, _COMMON),
+    "fa_decode_splitkv": (_I, _COMMON + [_I]),
+    "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "fa_decode_splitkv_ws": (_I, _COMMON + [_I, _P, _S]),
+    "fa_decode_auto_splits": (_I, [_I, _I, _I, _I]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_name(status)}): {detail}")
+
+
+def load():
+    """Load libfa_hip.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m exact_attention_54_amd.build` "
+                "(or __graft_entry__.build()) first"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def check(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where, last_error())

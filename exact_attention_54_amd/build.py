@@ -1,0 +1,80 @@
+"""Builds the gfx950 HIP library in-tree with hipcc.
+
+    python -m exact_attention_54_amd.build        # or __graft_entry__.build()
+
+Produces ``exact_attention_54_amd/libfa_hip.so`` from ``csrc/fa_api.hip``
+(the C ABI of ``include/fa.h`` plus every kernel) and the test-only MFMA
+layout probe ``tests/hip/libmfma_probe.so``.  Always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfa_hip.so")
+
+ARCH = "gfx950"
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # packed fp32 VALU forms are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    exe = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError(f"hipcc not found ({exe})")
+    return exe
+
+
+def compile_shared(sources, out, include_dirs=(), extra=(), verbose=False):
+    cmd = [hipcc(), *COMMON_FLAGS, *extra]
+    for d in include_dirs:
+        cmd += ["-I", d]
+    tmp = out + ".tmp"
+    cmd += list(sources) + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature name; that warning is expected
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, out)
+    return out
+
+
+PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
+
+
+def build_library(verbose: bool = False) -> str:
+    return compile_shared([os.path.join(CSRC, "fa_api.hip")], LIB, include_dirs=[INCLUDE, CSRC], verbose=verbose)
+
+
+def build_test_probe(verbose: bool = False) -> str:
+    """The MFMA lane-layout probe used by tests/test_mfma_probe.py."""
+    return compile_shared([PROBE_SRC], PROBE_LIB, verbose=verbose)
+
+
+def build_all(verbose: bool = False):
+    return [build_library(verbose), build_test_probe(verbose)]
+
+
+if __name__ == "__main__":
+    print(build_all(verbose="-v" in sys.argv))

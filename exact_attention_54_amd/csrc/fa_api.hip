@@ -1,0 +1,242 @@
+// Host side of the C ABI declared in include/fa.h: argument validation,
+// kernel selection, launch geometry and error reporting.  Every entry point
+// validates all arguments before its first HIP call.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa_decode_kernel.hpp"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a*b*c*d <= limit without overflow (all >= 1).
+bool product_le(int64_t a, int64_t b, int64_t c, int64_t d, int64_t limit) {
+  if (a > limit) return false;
+  int64_t p = a;
+  for (int64_t x : {b, c, d}) {
+    if (p > limit / x) return false;
+    p *= x;
+  }
+  return p <= limit;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, far above any HBM size
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+int validate(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+             int Sq, int Sk, int D, int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d Sq=%d Sk=%d D=%d)", B, H, Sq, Sk, D);
+  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!product_le(B, H, Sq, D, kMaxElems) || !product_le(B, H, Sk, D, kMaxElems))
+    return fail(FA_ERR_INVALID_ARG, "tensor too large");
+  return FA_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FA_OK;
+}
+
+int launched(const char* what) { return hip_check(hipGetLastError(), what); }
+
+template <int D, int BN, bool CAUSAL>
+int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+               float scale, hipStream_t stream) {
+  using Cfg = fa::FwdCfg<D, BN>;
+  const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
+  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  const float c2 = scale * fa::kLog2e;
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt, c2);
+  return launched("fa_fwd kernel launch");
+}
+
+template <int D>
+int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk,
+                  float scale, hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
+  const int chunk = (Sk + ns - 1) / ns;
+  const float c2 = scale * fa::kLog2e;
+  hipLaunchKernelGGL((fa::decode_partial_kernel<D>), dim3(BH * ns), dim3(fa::DecCfg<D>::THREADS), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                     static_cast<const _Float16*>(v), ws_o, ws_lse, Sk, ns, chunk, c2);
+  int rc = launched("decode phase-one launch");
+  if (rc != FA_OK) return rc;
+  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
+                     static_cast<_Float16*>(o), lse, ns);
+  return launched("decode merge launch");
+}
+
+std::atomic<int> g_cu_count[64];
+
+int device_cu_count(int* out) {
+  int dev = 0;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != FA_OK) return rc;
+  if (dev >= 0 && dev < 64) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return FA_OK;
+    }
+  }
+  int n = 0;
+  rc = hip_check(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev), "CU count query");
+  if (rc != FA_OK) return rc;
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return FA_OK;
+}
+
+size_t ws_bytes(int64_t BH, int D, int ns) {
+  const size_t floats = (size_t)BH * ns * (D + 1);
+  return (floats * 4 + 255) / 256 * 256;
+}
+
+int validate_decode(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+                    int Sq, int Sk, int D, int causal, float scale, int num_splits) {
+  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  if (Sq != 1) return fail(FA_ERR_INVALID_ARG, "split-KV decoding needs Sq == 1 (got %d)", Sq);
+  if (causal != 0) return fail(FA_ERR_INVALID_ARG, "split-KV decoding is non-causal");
+  if (num_splits > Sk) return fail(FA_ERR_INVALID_ARG, "num_splits %d exceeds Sk %d", num_splits, Sk);
+  if ((int64_t)B * H * (num_splits > 0 ? num_splits : 1) > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  return FA_OK;
+}
+
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk, int D,
+               float scale, hipStream_t stream, int ns, void* ws) {
+  float* ws_o = static_cast<float*>(ws);
+  float* ws_lse = ws_o + (size_t)BH * ns * D;
+  switch (D) {
+    case 64: return launch_decode<64>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
+    case 128: return launch_decode<128>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
+    default: return launch_decode<256>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
+  }
+}
+
+int resolve_splits(int B, int H, int Sk, int num_splits, int* ns) {
+  if (num_splits > 0) {
+    *ns = num_splits;
+    return FA_OK;
+  }
+  int cus = 0;
+  int rc = device_cu_count(&cus);
+  if (rc != FA_OK) return rc;
+  *ns = fa_decode_auto_splits(B, H, Sk, cus);
+  if (*ns < 1) return fail(FA_ERR_INVALID_ARG, "could not choose a split count");
+  if ((int64_t)B * H * *ns > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk, int D,
+           int causal, float scale, void* stream) {
+  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  const int BH = B * H;
+  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (D) {
+    case 64:
+      return causal ? launch_fwd<64, 64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd<64, 64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+    case 128:
+      return causal ? launch_fwd<128, 64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd<128, 64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+    default:
+      return causal ? launch_fwd<256, 32, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd<256, 32, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+  }
+}
+
+int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {
+  if (B < 1 || H < 1 || Sk < 1 || num_cus < 1) return 0;
+  const int64_t target = (int64_t)8 * num_cus;
+  const int64_t bh = (int64_t)B * H;
+  int64_t ns = 1;
+  while (bh * ns < target && ns < Sk) ns *= 2;
+  while (ns > 1 && (Sk + ns - 1) / ns < 256) ns /= 2;
+  if (ns > Sk) ns = Sk;
+  return (int)ns;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits) {
+  if (B < 1 || H < 1 || D < 1 || num_splits < 1) return 0;
+  return ws_bytes((int64_t)B * H, D, num_splits);
+}
+
+int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                         int Sk, int D, int causal, float scale, void* stream, int num_splits, void* workspace,
+                         size_t workspace_bytes) {
+  int rc = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, num_splits);
+  if (rc != FA_OK) return rc;
+  if (!workspace) return fail(FA_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int ns = 0;
+  rc = resolve_splits(B, H, Sk, num_splits, &ns);
+  if (rc != FA_OK) return rc;
+  const size_t need = ws_bytes((int64_t)B * H, D, ns);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  return run_decode(q, k, v, o, lse, B * H, Sk, D, scale, static_cast<hipStream_t>(stream), ns, workspace);
+}
+
+int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                      int Sk, int D, int causal, float scale, void* stream, int num_splits) {
+  int rc = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, num_splits);
+  if (rc != FA_OK) return rc;
+  int ns = 0;
+  rc = resolve_splits(B, H, Sk, num_splits, &ns);
+  if (rc != FA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = hip_check(hipMallocAsync(&ws, ws_bytes((int64_t)B * H, D, ns), s), "hipMallocAsync workspace");
+  if (rc != FA_OK) return rc;
+  rc = run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, ns, ws);
+  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
+  return rc != FA_OK ? rc : frc;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension";
+    case FA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The library computes exact (not approximate) softmax attention
+ *
+ *     O = softmax(scale * Q K^T + causal mask) V,   LSE_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * the way FlashAttention-2 organises it: one workgroup per query tile, key
+ * and value tiles streamed through LDS, an online softmax (running row max
+ * and row sum, rescaled as the max grows), the output accumulator kept in
+ * registers, and tiles above the causal diagonal skipped.  Sources:
+ *   - scores S = Q K^T / sqrt(d) and P = exp(S - m) / l:
+ *     "Adaptive High-Performance Attention Kernels in CUDA", Advanced
+ *     Production Features, 2. Custom CUDA Backward Pass;
+ *   - the running max / running sum recurrence: "FlashAttention-2 MMA",
+ *     Technical Details, Online Softmax (Safe Softmax);
+ *   - the causal rule key index <= query index: "FlashAttention-2 MMA",
+ *     Technical Details, Causal Masking;
+ *   - split-KV decoding (partial attention over key partitions, then a
+ *     log-sum-exp merge): "Adaptive High-Performance Attention Kernels in
+ *     CUDA", Advanced Production Features, 1. Split-K FlashDecoding, and
+ *     "FlashAttention-2 MMA", Supported Dispatch Strategies (Split-KV).
+ *
+ * Conventions shared by every entry point
+ *   Tensors   q, k, v, o are IEEE fp16, contiguous row-major [B, H, S, D]
+ *             (D innermost, then sequence, then head, then batch).  q and o
+ *             have S = Sq, k and v have S = Sk.  lse is fp32 [B, H, Sq].
+ *   Memory    every tensor pointer is device memory owned by the caller and
+ *             must stay valid until the stream has executed the call.
+ *             q, k, v, o must be 16-byte aligned, lse 4-byte aligned.  The
+ *             library keeps no pointer after it returns and never frees or
+ *             synchronises caller memory.
+ *   Stream    `stream` is a hipStream_t passed as void* (NULL = the null
+ *             stream).  Every call only enqueues work on that stream and
+ *             returns; results are valid once the stream has reached them.
+ *   Causal    top-left aligned: query row i sees keys 0..i (all keys when
+ *             i >= Sk), so no row is ever fully masked.
+ *   Scale     any finite scale > 0 (the pages use 1/sqrt(D)).
+ *   LSE       natural logarithm of the row sum of exp(scale * q . k) over the
+ *             visible keys.
+ *   Errors    a non-zero return is one of the FA_ERR_* codes.  Arguments are
+ *             validated on the host before any HIP call, so an invalid call
+ *             enqueues nothing.  FA_ERR_HIP reports a failed HIP launch or
+ *             allocation; fa_last_error() then names it.
+ *   Threads   calls hold no global mutable state apart from a per-device CU
+ *             count cache and a thread-local error message; they may be made
+ *             from several threads at once.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size out of range, bad scale, ... */
+  FA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256} */
+  FA_ERR_HIP = 3          /* a HIP call or kernel launch failed */
+};
+
+/*
+ * fa_fwd -- exact attention forward (prefill), FlashAttention-2 style.
+ *
+ *   q      [B, H, Sq, D] fp16        k, v  [B, H, Sk, D] fp16
+ *   o      [B, H, Sq, D] fp16 out    lse   [B, H, Sq]    fp32 out
+ *   B, H, Sq, Sk >= 1;  D in {64, 128, 256};  causal 0 or 1;  scale > 0.
+ *
+ * Queries are split into tiles, one workgroup each ("Split-Q" in
+ * "FlashAttention-2 MMA", Supported Dispatch Strategies; loop order of
+ * "Adaptive High-Performance Attention Kernels in CUDA", Architectural
+ * Progression, Stage 3).  With causal = 1 the key tiles that lie wholly
+ * above the diagonal are never loaded (same page, Lever A).  Any Sq works,
+ * including Sq = 1.  o and lse must not overlap the inputs.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Sq, int Sk, int D, int causal, float scale,
+           void* stream);
+
+/*
+ * fa_decode_splitkv -- single-query decoding with the key range split into
+ * num_splits contiguous partitions ("Adaptive High-Performance Attention
+ * Kernels in CUDA", Advanced Production Features, 1. Split-K FlashDecoding).
+ *
+ * Same arguments as fa_fwd plus num_splits; requires Sq == 1 and causal == 0
+ * (FA_ERR_INVALID_ARG otherwise).  Partition s covers keys
+ * [s*c, min((s+1)*c, Sk)) with c = ceil(Sk / num_splits); trailing
+ * partitions may be empty.  num_splits <= 0 picks fa_decode_auto_splits()
+ * for the current device; otherwise 1 <= num_splits <= Sk.
+ * Phase one writes a normalised partial output and its LSE per partition;
+ * phase two merges them with log-sum-exp weights into o and lse.  Both
+ * kernels run on `stream`.  The partials live in a workspace obtained with
+ * hipMallocAsync on `stream` and released with hipFreeAsync on the same
+ * stream after phase two (stream-ordered, so nothing blocks).
+ */
+int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                      void* stream, int num_splits);
+
+/*
+ * fa_decode_workspace_bytes -- bytes of workspace fa_decode_splitkv_ws needs
+ * for these sizes: B*H*num_splits*(D + 1) fp32 values, rounded up to 256.
+ * num_splits must be >= 1 (use fa_decode_auto_splits first for "auto").
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits);
+
+/*
+ * fa_decode_splitkv_ws -- fa_decode_splitkv with a caller-provided device
+ * workspace (at least fa_decode_workspace_bytes(B, H, D, ns) bytes, 16-byte
+ * aligned, where ns is the resolved split count).  Nothing is allocated.
+ * On return the workspace is laid out as partial outputs fp32
+ * [B, H, ns, D] followed by partial LSEs fp32 [B, H, ns] (natural log;
+ * -inf for an empty partition, whose partial output is 0).  Calls that
+ * share one workspace must be ordered on one stream.
+ */
+int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                         void* stream, int num_splits, void* workspace, size_t workspace_bytes);
+
+/*
+ * fa_decode_auto_splits -- the split count fa_decode_splitkv uses when
+ * num_splits <= 0: the smallest power of two that gives at least
+ * 8 * num_cus phase-one workgroups, lowered until every partition holds at
+ * least 256 keys (never below 1, never above Sk).  Pure host arithmetic;
+ * returns 0 for invalid sizes.
+ */
+int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
+
+/* fa_status_string -- static text for an FA_* status code. */
+const char* fa_status_string(int status);
+
+/* fa_last_error -- text of the last FA_ERR_* raised on this thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,162 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects invalid arguments before any HIP call
+(the fake pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_54_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x10000  # 16-byte aligned fake device addresses
+P = [A, A + 0x1000, A + 0x2000, A + 0x3000, A + 0x4000]
+GOOD = dict(B=2, H=3, Sq=5, Sk=7, D=64, causal=0, scale=0.125)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _capi.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert names == sorted(_capi.SIGNATURES), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def fwd(lib, p=P, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_fwd(p[0], p[1], p[2], p[3], p[4], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["causal"],
+                      a["scale"], None)
+
+
+def dec(lib, p=P, ns=2, **kw):
+    a = dict(GOOD, Sq=1)
+    a.update(kw)
+    return lib.fa_decode_splitkv(p[0], p[1], p[2], p[3], p[4], a["B"], a["H"], a["Sq"], a["Sk"], a["D"],
+                                 a["causal"], a["scale"], None, ns)
+
+
+def dec_ws(lib, ws=A + 0x8000, nbytes=1 << 20, p=P, ns=2, **kw):
+    a = dict(GOOD, Sq=1)
+    a.update(kw)
+    return lib.fa_decode_splitkv_ws(p[0], p[1], p[2], p[3], p[4], a["B"], a["H"], a["Sq"], a["Sk"], a["D"],
+                                    a["causal"], a["scale"], None, ns, ws, nbytes)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(H=-1), _capi.FA_ERR_INVALID_ARG),
+    (dict(Sq=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(Sk=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(D=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(D=96), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=32), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=512), _capi.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), _capi.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _capi.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), _capi.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _capi.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _capi.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 20, H=1 << 20, Sq=1 << 10, D=64), _capi.FA_ERR_INVALID_ARG),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert _capi.last_error() != ""
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_fwd_rejects_null(lib, idx):
+    p = list(P)
+    p[idx] = None
+    assert fwd(lib, p=p) == _capi.FA_ERR_INVALID_ARG
+    assert "null" in _capi.last_error()
+
+
+@pytest.mark.parametrize("idx,off", [(0, 8), (1, 4), (2, 2), (3, 8), (4, 2)])
+def test_fwd_rejects_misaligned(lib, idx, off):
+    p = list(P)
+    p[idx] += off
+    assert fwd(lib, p=p) == _capi.FA_ERR_INVALID_ARG
+    assert "aligned" in _capi.last_error()
+
+
+def test_lse_needs_only_4_byte_alignment_check(lib):
+    # lse at +4 passes alignment; use an invalid D so no HIP call happens
+    p = list(P)
+    p[4] += 4
+    assert fwd(lib, p=p, D=96) == _capi.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,ns", [
+    (dict(Sq=2), 2),
+    (dict(causal=1), 2),
+    (dict(Sk=7), 8),
+    (dict(D=96), 2),
+    (dict(scale=-1.0), 2),
+])
+def test_decode_rejects(lib, kw, ns):
+    code = _capi.FA_ERR_UNSUPPORTED if kw.get("D") == 96 else _capi.FA_ERR_INVALID_ARG
+    a = dict(kw)
+    sq = a.pop("Sq", 1)
+    assert lib.fa_decode_splitkv(P[0], P[1], P[2], P[3], P[4], GOOD["B"], GOOD["H"], sq, a.get("Sk", GOOD["Sk"]),
+                                 a.get("D", 64), a.get("causal", 0), a.get("scale", 0.125), None, ns) == code
+
+
+def test_decode_ws_rejects(lib):
+    need = lib.fa_decode_workspace_bytes(2, 3, 64, 2)
+    assert dec_ws(lib, ws=None) == _capi.FA_ERR_INVALID_ARG
+    assert dec_ws(lib, ws=A + 0x8008) == _capi.FA_ERR_INVALID_ARG
+    assert dec_ws(lib, nbytes=need - 1) == _capi.FA_ERR_INVALID_ARG
+    assert "workspace" in _capi.last_error()
+    assert dec_ws(lib, Sq=3) == _capi.FA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_decode_workspace_bytes(16, 32, 128, 4) == 16 * 32 * 4 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 64, 3) == 1024  # 195 floats -> 780 B -> 1024
+    assert lib.fa_decode_workspace_bytes(0, 1, 64, 3) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 64, 0) == 0
+
+
+@pytest.mark.parametrize("B,H,Sk,cus,want", [
+    (16, 32, 8192, 256, 4),     # 512 slices x 4 = 2048 workgroups = 8 per CU
+    (1, 1, 8192, 256, 32),      # capped so each partition keeps >= 256 keys
+    (1, 1, 100, 256, 1),
+    (1, 1, 1, 256, 1),
+    (64, 64, 8192, 256, 1),     # already 16 workgroups per CU
+    (2, 8, 4096, 304, 16),
+    (0, 1, 10, 256, 0),
+    (1, 1, 10, 0, 0),
+])
+def test_auto_splits(lib, B, H, Sk, cus, want):
+    assert lib.fa_decode_auto_splits(B, H, Sk, cus) == want
+
+
+def test_status_strings(lib):
+    assert _capi.status_name(0) == "ok"
+    assert _capi.status_name(1) == "invalid argument"
+    assert _capi.status_name(2) == "unsupported head dimension"
+    assert _capi.status_name(3) == "HIP error"
+    assert _capi.status_name(99) == "unknown status"
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import exact_attention_54_amd as fa
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fa_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(q.float(), q, q)

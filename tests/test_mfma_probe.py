@@ -1,0 +1,48 @@
+"""Pins the 32x32x16 fp16 MFMA lane layout the kernels assume (GPU).
+
+Lane l supplies A[l % 32][8 * (l // 32) + t] and B[8 * (l // 32) + t][l % 32]
+(t = 0..7) and receives C[8 * (j // 4) + 4 * (l // 32) + j % 4][l % 32] in
+accumulator register j.  Small-integer operands make every product exact.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+PROBE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libmfma_probe.so")
+
+
+def test_mfma_32x32x16_layout():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU test needs a GPU"
+    assert os.path.exists(PROBE), "probe library not built"
+    lib = ctypes.CDLL(PROBE)
+    lib.probe_mfma_32x32x16.restype = ctypes.c_int
+    lib.probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 3
+
+    rng = np.random.Generator(np.random.PCG64(7))
+    A = rng.integers(-8, 9, size=(32, 16)).astype(np.float16)
+    B = rng.integers(-8, 9, size=(16, 32)).astype(np.float16)
+    a_regs = np.empty((64, 8), np.float16)
+    b_regs = np.empty((64, 8), np.float16)
+    for l in range(64):
+        for t in range(8):
+            a_regs[l, t] = A[l % 32, 8 * (l // 32) + t]
+            b_regs[l, t] = B[8 * (l // 32) + t, l % 32]
+    dev = torch.device("cuda:0")
+    a_d = torch.from_numpy(a_regs).to(dev)
+    b_d = torch.from_numpy(b_regs).to(dev)
+    c_d = torch.zeros((64, 16), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    assert lib.probe_mfma_32x32x16(a_d.data_ptr(), b_d.data_ptr(), c_d.data_ptr()) == 0
+    c_regs = c_d.cpu().numpy()
+    C = A.astype(np.float64) @ B.astype(np.float64)
+    got = np.empty((32, 32))
+    for l in range(64):
+        for j in range(16):
+            got[8 * (j // 4) + 4 * (l // 32) + j % 4, l % 32] = c_regs[l, j]
+    np.testing.assert_array_equal(got, C)
