@@ -41,6 +41,7 @@ bool product_le(int64_t a, int64_t b, int64_t c, int64_t d, int64_t limit) {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, far above any HBM size
 constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;
 
 int validate(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
              int Sq, int Sk, int D, int causal, float scale) {
@@ -55,6 +56,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (!product_le(B, H, Sq, D, kMaxElems) || !product_le(B, H, Sk, D, kMaxElems))
     return fail(FA_ERR_INVALID_ARG, "tensor too large");
+  // one (batch, head) slice is addressed with 32-bit byte offsets
+  if ((int64_t)Sq * D * 2 >= kMaxSliceBytes || (int64_t)Sk * D * 2 >= kMaxSliceBytes)
+    return fail(FA_ERR_INVALID_ARG, "sequence too long: one [S, D] slice must stay below 2 GiB");
   return FA_OK;
 }
 

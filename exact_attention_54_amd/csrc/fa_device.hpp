@@ -49,11 +49,100 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
   }
 }
 
+// Inverse of swz<C>: the (row, chunk) stored at 16-byte slot `slot` of
+// 256-byte line `line`.
+template <int C>
+__device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
+  if constexpr (C >= 16) {
+    r = line / (C / 16);
+    c = (line % (C / 16)) * 16 + (slot ^ (r & 15));
+  } else {
+    constexpr int RPL = 16 / C;
+    r = line * RPL + slot / C;
+    c = (slot % C) ^ (line & (C - 1));
+  }
+}
+
+// Row-major [key][d] layout for V tiles read with ds_read_b64_tr_b16: a
+// transposed read touches 4 consecutive key rows x 4 consecutive 16-byte
+// chunks, and the XOR below spreads those 16 chunks over the 16 bank groups
+// of a 256-byte line.
+template <int C>
+__device__ __forceinline__ uint32_t vswz(int r, int c) {
+  static_assert(C == 8 || C == 16 || C == 32, "chunks per row");
+  if constexpr (C >= 16) {
+    const int line = r * (C / 16) + (c >> 4);
+    const int slot = (c & 15) ^ (4 * (r & 3));
+    return (uint32_t)(line * 256 + slot * 16);
+  } else {
+    const int line = r >> 1;
+    const int slot = (r & 1) * 8 + (c ^ (4 * (line & 1)));
+    return (uint32_t)(line * 256 + slot * 16);
+  }
+}
+template <int C>
+__device__ __forceinline__ void vswz_inv(int line, int slot, int& r, int& c) {
+  if constexpr (C >= 16) {
+    r = line / (C / 16);
+    c = (line % (C / 16)) * 16 + (slot ^ (4 * (r & 3)));
+  } else {
+    r = line * 2 + slot / 8;
+    c = (slot % 8) ^ (4 * (line & 1));
+  }
+}
+
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte blocks addressed by group lanes i / 4 + 4 j, j = 0..3.
+// So if group lane 4 j + a points at row key_j, columns d0 + 4 a .. + 3 of
+// a row-major array, lane i gets column d0 + i of rows key_0..key_3.
+__device__ __forceinline__ h4v lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(h4v, v);
+}
+
+// 16-byte global -> LDS copy per lane through a buffer resource.  The LDS
+// destination of lane l is lds_base + 16 l (lds_base is wave-uniform); a
+// load past the buffer's end writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
+}
+
 // Maximum / sum of x over the two 32-lane halves of a wavefront.
 __device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
 
 __device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end read
+// 0 and stores past the end are dropped by the address unit, which is how
+// the kernels handle ragged sequence tails without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// sum += a.x * b.x + a.y * b.y in fp32 (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(h2 a, h2 b, float sum) { return __builtin_amdgcn_fdot2(a, b, sum, false); }
+
+// Waits until every vector-memory load of this wavefront has returned
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).  Placed
+// before a loop, it tells the compiler's wait-count tracking that loads
+// issued earlier need no waits inside the loop.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// True on every lane if pred holds on any lane of the wavefront.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 // Packs the low (hi_half = false) or high halves of two dwords: result low
 // 16 bits from a, high 16 bits from b.

@@ -12,26 +12,33 @@
 //                 transposed product puts one query row in each lane (lanes
 //                 l and l+32 share a row), so the row max needs one
 //                 cross-half exchange and the row sum none until the end.
-//   online softmax  m_new = max(m, rowmax), p = 2^(s*c - m_new),
-//                 alpha = 2^(m - m_new), l = alpha*l + rowsum(p), O *= alpha,
+//   online softmax  m_new = max(m, rowmax), p = 2^(s*c - m), l += rowsum(p),
 //                 with c = scale*log2(e) folded into one FMA per score
 //                 ("FlashAttention-2 MMA", Technical Details, Online Softmax).
+//                 The reference max m only moves when a row max grows by
+//                 more than 2^8 (then O and l are rescaled by 2^(m - m_new));
+//                 in between p <= 2^8, which fp16 and fp32 hold exactly, so
+//                 the result is unchanged and the rescale is rare.
 //   O^T += V^T P^T  P is rounded to fp16 in registers and used directly as
 //                 the B operand: the accumulator layout of S^T lists keys
 //                 8*(j/4) + 4*(l/32) + j%4, and the contraction index is
-//                 free to permute as long as V^T uses the same order, so V
-//                 is written to LDS transposed ([d][key]) with key bits 2
-//                 and 3 swapped; each lane then reads its 8 keys as one
-//                 16-byte LDS load.
-// Key/value tiles are double-buffered in LDS: the next tile's global loads
-// (16-byte, coalesced) are issued before the current tile's MFMAs and
-// written to the other LDS stage afterwards (Lever C of the same page).
-// Both LDS arrays use the XOR swizzle of fa::swz (Lever B).
+//                 free to permute as long as V^T uses the same order.  V
+//                 stays row-major in LDS and each lane gathers its 8 keys of
+//                 one d column with two ds_read_b64_tr_b16.
+// Data movement: K and V tiles go straight from HBM to LDS with 16-byte
+// buffer loads (no register staging), double-buffered, K one tile ahead of
+// V (Lever C of the same page).  Both LDS arrays are XOR-swizzled (Lever B):
+// K for the 32-row column reads of the A operand, V for the transposed reads.
+// Software pipeline inside each wavefront: the MFMAs of S(j+1) are issued in
+// the same basic block as the exp/convert/sum work of tile j, so the matrix
+// core and the vector ALU run concurrently, then P(j) V(j) follows.
 // Causal: key tiles wholly above the diagonal of the workgroup are never
-// visited, wavefronts skip tiles above their own rows, and only tiles that
+// loaded, wavefronts skip tiles above their own rows, and only tiles that
 // cross the diagonal evaluate the mask (Lever A).  Query tiles are issued
 // heaviest first so the triangular work packs well onto the CUs.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_device.hpp"
 
@@ -42,30 +49,31 @@ struct FwdCfg {
   static constexpr int NWAVES = 4;
   static constexpr int THREADS = 64 * NWAVES;
   static constexpr int BM = 32 * NWAVES;
-  static constexpr int KCH = D / 8;   // 16-byte chunks per K row in LDS
-  static constexpr int VCH = BN / 8;  // 16-byte chunks per V^T row in LDS
-  static constexpr int NKB = BN / 32; // 32-key blocks per tile
-  static constexpr int NDB = D / 32;  // 32-wide d blocks of the output
-  static constexpr int K_TILE_BYTES = BN * D * 2;
-  static constexpr int V_TILE_BYTES = D * BN * 2;
-  static constexpr int STAGE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
+  static constexpr int KCH = D / 8;    // 16-byte chunks per K / V row
+  static constexpr int NKB = BN / 32;  // 32-key blocks per tile
+  static constexpr int NDB = D / 32;   // 32-wide d blocks of the output
+  static constexpr int KS = D / 16;    // k-steps of S = K Q^T
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int LPW = TILE_BYTES / 1024 / NWAVES;  // 1 KiB LDS loads per wavefront per tile
+  static constexpr int V_BASE = 2 * TILE_BYTES;           // LDS: K0 K1 V0 V1
   static constexpr int EPI_BYTES = NWAVES * 32 * D * 2;
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > EPI_BYTES) ? 2 * STAGE_BYTES : EPI_BYTES;
-  static constexpr int K_PER_THREAD = BN * KCH / THREADS;     // 16-byte K chunks per thread
-  static constexpr int V_BLOCKS = (BN / 4) * (D / 8);          // 4-key x 8-d V blocks per tile
-  static constexpr int V_PER_THREAD = (V_BLOCKS + THREADS - 1) / THREADS;
+  static constexpr int LDS_BYTES = (4 * TILE_BYTES > EPI_BYTES) ? 4 * TILE_BYTES : EPI_BYTES;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(BN * KCH % THREADS == 0, "K tile must split evenly over the workgroup");
+  static_assert(TILE_BYTES % (1024 * NWAVES) == 0, "tile must split into 1 KiB loads per wavefront");
   static_assert(LDS_BYTES <= 65536, "static LDS budget");
 };
 
-// Position of key `k` (0..BN-1) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+// Row-max growth (log2 units) tolerated before the reference max moves.
+constexpr float kLazyRescale = 8.0f;
+
+// Workgroups per CU the register budget is sized for: two at D <= 128, so
+// one workgroup's softmax overlaps the other's MFMAs; one at D = 256, whose
+// 32 x 256 fp32 accumulator per wavefront needs the whole register file.
+template <int D>
+constexpr int fwd_wg_per_cu() { return D <= 128 ? 2 : 1; }
 
 template <int D, int BN, bool CAUSAL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, fwd_wg_per_cu<D>())
 fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
            const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
            int Sq, int Sk, int BH, int nqt, float c2) {
@@ -87,164 +95,184 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   const int bh = blockIdx.x - rank * BH;
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const int q0 = qt * C::BM;
-  const int qw = q0 + 32 * w;            // first query row of this wavefront
-  const int qi = qw + r32;               // query row held by this lane
-  const size_t qoff = (size_t)bh * Sq * D;
-  const size_t koff = (size_t)bh * Sk * D;
+  const int qw = q0 + 32 * w;  // first query row of this wavefront
+  const int qi = qw + r32;     // query row held by this lane
+
+  // Per-slice buffer resources: rows past Sq / Sk read as zero and stores
+  // past Sq are dropped.
+  const auto rq = make_rsrc(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  const auto rk = make_rsrc(K + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
+  const auto rv = make_rsrc(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
+  const auto ro = make_rsrc(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
 
   // Q fragment: B operand of S^T = K Q^T, 8 consecutive d per lane and step.
-  h8 qreg[D / 16];
+  h8 qreg[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (qi < Sq) t = *reinterpret_cast<const u32x4*>(Q + qoff + (size_t)qi * D + 16 * ks + 8 * hh);
-    qreg[ks] = as_h8(t);
-  }
+  for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_h8(buf_load16(rq, ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u));
 
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + C::BM, Sk) + BN - 1) / BN) : nkt_all;
+  // last key tile this wavefront needs (-1: none, its rows are all past Sq)
+  const int jlast = (qw >= Sq) ? -1 : (CAUSAL ? min(nkt - 1, (qw + 31) / BN) : nkt - 1);
 
-  // Global -> register staging of one K/V tile.
-  u32x4 kst[C::K_PER_THREAD];
-  u32x4 vst[C::V_PER_THREAD][4];
-  auto gload = [&](int kt) {
-    const int kbase = kt * BN;
+  // Global byte offsets (inside one tile) of the 16-byte chunks this lane
+  // moves into LDS: wavefront w fills 1 KiB blocks w*LPW .. w*LPW+LPW-1 of
+  // each stage, lane l the 16 bytes at 16*l, and the chunk that belongs
+  // there is found through the inverse swizzle.
+  uint32_t kgo[C::LPW], vgo[C::LPW];
 #pragma unroll
-    for (int u = 0; u < C::K_PER_THREAD; ++u) {
-      const int ci = tid + C::THREADS * u;
-      const int r = ci / C::KCH, c = ci % C::KCH;
-      const int key = kbase + r;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (key < Sk) t = *reinterpret_cast<const u32x4*>(K + koff + (size_t)key * D + c * 8);
-      kst[u] = t;
-    }
+  for (int u = 0; u < C::LPW; ++u) {
+    const int p = (w * C::LPW + u) * 1024 + lane * 16;
+    int r, c;
+    swz_inv<C::KCH>(p >> 8, (p >> 4) & 15, r, c);
+    kgo[u] = (uint32_t)(r * D + c * 8) * 2;
+    vswz_inv<C::KCH>(p >> 8, (p >> 4) & 15, r, c);
+    vgo[u] = (uint32_t)(r * D + c * 8) * 2;
+  }
+  auto load_k = [&](int kt, int stage) {
+    const uint32_t tb = (uint32_t)kt * C::TILE_BYTES;
 #pragma unroll
-    for (int u = 0; u < C::V_PER_THREAD; ++u) {
-      const int bi = tid + C::THREADS * u;
-      if (C::V_BLOCKS % C::THREADS != 0 && bi >= C::V_BLOCKS) continue;
-      const int kg = bi / (D / 8), dc = bi % (D / 8);
+    for (int u = 0; u < C::LPW; ++u)
+      buf_load16_lds(rk, smem + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + kgo[u]);
+  };
+  auto load_v = [&](int kt, int stage) {
+    const uint32_t tb = (uint32_t)kt * C::TILE_BYTES;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = kbase + 4 * kg + rr;
-        u32x4 t = {0u, 0u, 0u, 0u};
-        if (key < Sk) t = *reinterpret_cast<const u32x4*>(V + koff + (size_t)key * D + dc * 8);
-        vst[u][rr] = t;
+    for (int u = 0; u < C::LPW; ++u)
+      buf_load16_lds(rv, smem + C::V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
+  };
+
+  // S^T = K Q^T for the tile in K stage `stage`.
+  auto qk = [&](int stage, f32x16 (&s)[C::NKB]) {
+    const char* Ks = smem + stage * C::TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const h8 a = *reinterpret_cast<const h8*>(Ks + swz<C::KCH>(32 * kb + r32, 2 * ks + hh));
+        s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
     }
   };
-  // Register -> LDS stage: K row-major swizzled, V transposed to [d][key].
-  auto lstore = [&](int st) {
-    char* Ks = smem + st * C::STAGE_BYTES;
-    char* Vs = Ks + C::K_TILE_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::K_PER_THREAD; ++u) {
-      const int ci = tid + C::THREADS * u;
-      const int r = ci / C::KCH, c = ci % C::KCH;
-      *reinterpret_cast<u32x4*>(Ks + swz<C::KCH>(r, c)) = kst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_PER_THREAD; ++u) {
-      const int bi = tid + C::THREADS * u;
-      if (C::V_BLOCKS % C::THREADS != 0 && bi >= C::V_BLOCKS) continue;
-      const int kg = bi / (D / 8), dc = bi % (D / 8);
-      const int p = vt_pos(4 * kg);         // 4 consecutive keys stay consecutive
-      const int cp = p >> 3, hoff = (p & 7) * 2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        const bool hi = (e & 1) != 0;
-        u32x2 out;
-        out.x = pack_halves(vst[u][0][dw], vst[u][1][dw], hi);
-        out.y = pack_halves(vst[u][2][dw], vst[u][3][dw], hi);
-        *reinterpret_cast<u32x2*>(Vs + swz<C::VCH>(8 * dc + e, cp) + hoff) = out;
-      }
-    }
-  };
+
+  // Lane constants of the transposed V reads: key offset i/4 inside the
+  // 4-key group, 16-byte chunk and 8-byte half of column 16*(g%2) + 4*(i%4).
+  const int ti = lane & 15;
+  const int tg = (lane >> 4) & 1;
+  const int v_key = 4 * hh + (ti >> 2);
+  const int v_chunk = 2 * tg + ((ti & 3) >> 1);
+  const int v_half = (ti & 1) * 8;
 
   f32x16 oacc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
-  float m_run = kNegInf;  // running row max of s*c (log2 units)
-  float l_run = 0.f;      // this lane's share of the running row sum
+  float m_run = kNegInf;  // reference max of s*c (log2 units) of this lane's row
+  float m_cand = kNegInf; // reference max wanted by the next tile
+  bool grow = false;      // m_cand > m_run: O and l need the rescale first
+  float l_run = 0.f;      // this lane's share of the row sum
+  f32x16 s_cur[C::NKB];
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-
-    const int kbase = kt * BN;
-    const bool active = (qw < Sq) && (!CAUSAL || kbase <= qw + 31);
-    if (active) {
-      const char* Ks = smem + st * C::STAGE_BYTES;
-      const char* Vs = Ks + C::K_TILE_BYTES;
-
-      f32x16 sacc[C::NKB];
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const h8 a = *reinterpret_cast<const h8*>(Ks + swz<C::KCH>(32 * kb + r32, 2 * ks + hh));
-          sacc[kb] = mfma_32x32x16(a, qreg[ks], sacc[kb]);
-        }
-      }
-
-      const bool need_mask = (kbase + BN > Sk) || (CAUSAL && kbase + BN - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = kbase + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (key >= Sk || (CAUSAL && key > qi)) sacc[kb][j] = kNegInf;
-          }
-      }
-
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-
-      h8 pop[C::NKB][2];
-      float psum = 0.f;
+  // Masks S^T of key tile kt (keys past Sk, and keys after the row when
+  // causal), then decides whether the reference max must move for it.
+  auto mask_and_max = [&](f32x16 (&s)[C::NKB], int kt, bool mask) {
+    if (mask) {
+      const int kbase = kt * BN;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float p = exp2_fast(__builtin_fmaf(sacc[kb][j], c2, -m_use));
-          psum += p;
-          pop[kb][j >> 3][j & 7] = (_Float16)p;
+          const int key = kbase + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (key >= Sk || (CAUSAL && key > qi)) s[kb][j] = kNegInf;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const h8 a = *reinterpret_cast<const h8*>(Vs + swz<C::VCH>(32 * db + r32, 4 * kb + 2 * k2 + hh));
-            oacc[db] = mfma_32x32x16(a, pop[kb][k2], oacc[db]);
-          }
     }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[kb][j]), s[kb][j + 1]);  // v_max3
+    const float mt = xhalf_max(mx) * c2;
+    grow = mt > m_run + kLazyRescale;
+    m_cand = grow ? mt : m_run;
+  };
 
-    if (kt + 1 < nkt) lstore(st ^ 1);
+  // One pipelined step on tile kt, a single basic block: exp/convert/sum of
+  // S(kt) issued together with the MFMAs of S(kt+1) (when NEXT), then
+  // O += P(kt) V(kt) issued together with the mask and row max of S(kt+1).
+  auto step = [&](int kt, bool mask_next, auto next_tag) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    h8 pop[C::NKB][2];
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        h2 pr;
+        pr[0] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[kb][j], c2, -m_use));
+        pr[1] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[kb][j + 1], c2, -m_use));
+        l_run = dot2(pr, ones, l_run);  // row sum of the fp16 P that feeds P V
+        pop[kb][j >> 3][j & 7] = pr[0];
+        pop[kb][j >> 3][(j & 7) + 1] = pr[1];
+      }
+    f32x16 s_nxt[C::NKB];
+    if constexpr (NEXT) qk((kt + 1) & 1, s_nxt);
+
+    const char* Vs = smem + C::V_BASE + (kt & 1) * C::TILE_BYTES;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int key = 32 * kb + 16 * k2 + v_key;
+          const int chunk = 4 * db + v_chunk;
+          const h4v lo = lds_read_tr16(Vs + vswz<C::KCH>(key, chunk) + v_half);
+          const h4v hi = lds_read_tr16(Vs + vswz<C::KCH>(key + 8, chunk) + v_half);
+          const h8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[db] = mfma_32x32x16(a, pop[kb][k2], oacc[db]);
+        }
+    if constexpr (NEXT) {
+      mask_and_max(s_nxt, kt + 1, mask_next);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_nxt[kb];
+    }
+  };
+  auto tile_needs_mask = [&](int kt) { return (kt * BN + BN > Sk) || (CAUSAL && kt * BN + BN - 1 > qw); };
+
+  // Prologue: K(0), V(0), K(1) resident, S(0) computed, masked and maxed.
+  load_k(0, 0);
+  load_v(0, 0);
+  if (nkt > 1) load_k(1, 1);
+  wait_vmem_all();
+  __syncthreads();
+  if (jlast >= 0) {
+    qk(0, s_cur);
+    mask_and_max(s_cur, 0, tile_needs_mask(0));
+  }
+  __syncthreads();  // K stage 0 is refilled with K(2) below
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 2 < nkt) load_k(kt + 2, kt & 1);
+    if (kt + 1 < nkt) load_v(kt + 1, (kt + 1) & 1);
+    if (kt <= jlast) {
+      if (wave_any(grow)) {  // rare: some row max grew by more than 2^8
+        const float alpha = exp2_fast(m_run - m_cand);  // 1 where the max stays, 0 on a row's first tile
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        m_run = m_cand;
+        grow = false;
+      }
+      if (kt + 1 < nkt) step(kt, tile_needs_mask(kt + 1), std::true_type{});
+      else step(kt, false, std::false_type{});
+    }
+    wait_vmem_all();
     __syncthreads();
   }
 
@@ -266,14 +294,14 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       *reinterpret_cast<h4*>(Os + swz<C::KCH>(r32, d0 >> 3) + (d0 & 7) * 2) = val;
     }
   __syncthreads();
+  if (qw < Sq) {
 #pragma unroll
-  for (int u = 0; u < (32 * D / 8) / 64; ++u) {
-    const int ci = lane + 64 * u;
-    const int row = ci / C::KCH, c = ci % C::KCH;
-    const int qrow = qw + row;
-    if (qrow < Sq)
-      *reinterpret_cast<u32x4*>(O + qoff + (size_t)qrow * D + c * 8) =
-          *reinterpret_cast<const u32x4*>(Os + swz<C::KCH>(row, c));
+    for (int u = 0; u < (32 * D / 8) / 64; ++u) {
+      const int ci = lane + 64 * u;
+      const int row = ci / C::KCH, c = ci % C::KCH;
+      buf_store16(ro, ((uint32_t)(qw + row) * D + c * 8) * 2u,
+                  *reinterpret_cast<const u32x4*>(Os + swz<C::KCH>(row, c)));
+    }
   }
   if (hh == 0 && qi < Sq) LSE[(size_t)bh * Sq + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
 }

@@ -36,6 +36,8 @@
  *   Causal    top-left aligned: query row i sees keys 0..i (all keys when
  *             i >= Sk), so no row is ever fully masked.
  *   Scale     any finite scale > 0 (the pages use 1/sqrt(D)).
+ *   Limits    one [S, D] slice of q, k, v or o must stay below 2 GiB
+ *             (S * D * 2 < 2^31 bytes); the tensors as a whole may be larger.
  *   LSE       natural logarithm of the row sum of exp(scale * q . k) over the
  *             visible keys.
  *   Errors    a non-zero return is one of the FA_ERR_* codes.  Arguments are
