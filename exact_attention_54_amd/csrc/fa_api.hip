@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -118,6 +119,39 @@ int device_cu_count(int* out) {
   return FA_OK;
 }
 
+// One stream-ordered memory pool per device for decode workspaces.  Its
+// release threshold is unlimited, so memory freed with hipFreeAsync stays in
+// the pool and the next call reuses it without going back to the driver.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices] = {};
+
+int workspace_pool(hipMemPool_t* out) {
+  int dev = 0;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != FA_OK) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    rc = hip_check(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate");
+    if (rc != FA_OK) return rc;
+    uint64_t keep = UINT64_MAX;
+    rc = hip_check(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep), "pool release threshold");
+    if (rc != FA_OK) {
+      hipMemPoolDestroy(pool);
+      return rc;
+    }
+    g_pool[dev] = pool;
+  }
+  *out = g_pool[dev];
+  return FA_OK;
+}
+
 size_t ws_bytes(int64_t BH, int D, int ns) {
   const size_t floats = (size_t)BH * ns * (D + 1);
   return (floats * 4 + 255) / 256 * 256;
@@ -223,8 +257,11 @@ int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, floa
   rc = resolve_splits(B, H, Sk, num_splits, &ns);
   if (rc != FA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipMemPool_t pool = nullptr;
+  rc = workspace_pool(&pool);
+  if (rc != FA_OK) return rc;
   void* ws = nullptr;
-  rc = hip_check(hipMallocAsync(&ws, ws_bytes((int64_t)B * H, D, ns), s), "hipMallocAsync workspace");
+  rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)B * H, D, ns), pool, s), "workspace allocation");
   if (rc != FA_OK) return rc;
   rc = run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, ns, ws);
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");

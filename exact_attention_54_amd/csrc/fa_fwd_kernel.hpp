@@ -82,7 +82,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave branches stay scalar
   const int r32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -177,9 +177,10 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   f32x16 s_cur[C::NKB];
 
   // Masks S^T of key tile kt (keys past Sk, and keys after the row when
-  // causal), then decides whether the reference max must move for it.
-  auto mask_and_max = [&](f32x16 (&s)[C::NKB], int kt, bool mask) {
-    if (mask) {
+  // causal; only instantiated for tiles that need it), then decides whether
+  // the reference max must move for it.
+  auto mask_and_max = [&](f32x16 (&s)[C::NKB], int kt, auto mask_tag) {
+    if constexpr (decltype(mask_tag)::value) {
       const int kbase = kt * BN;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -202,7 +203,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // One pipelined step on tile kt, a single basic block: exp/convert/sum of
   // S(kt) issued together with the MFMAs of S(kt+1) (when NEXT), then
   // O += P(kt) V(kt) issued together with the mask and row max of S(kt+1).
-  auto step = [&](int kt, bool mask_next, auto next_tag) {
+  auto step = [&](int kt, auto mask_next, auto next_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     h8 pop[C::NKB][2];
@@ -251,7 +252,8 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   __syncthreads();
   if (jlast >= 0) {
     qk(0, s_cur);
-    mask_and_max(s_cur, 0, tile_needs_mask(0));
+    if (tile_needs_mask(0)) mask_and_max(s_cur, 0, std::true_type{});
+    else mask_and_max(s_cur, 0, std::false_type{});
   }
   __syncthreads();  // K stage 0 is refilled with K(2) below
 
@@ -269,8 +271,14 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         m_run = m_cand;
         grow = false;
       }
-      if (kt + 1 < nkt) step(kt, tile_needs_mask(kt + 1), std::true_type{});
-      else step(kt, false, std::false_type{});
+      // the mask of S(kt+1) is a compile-time variant, so unmasked tiles
+      // carry no compare/select work
+      if (kt + 1 < nkt) {
+        if (tile_needs_mask(kt + 1)) step(kt, std::true_type{}, std::true_type{});
+        else step(kt, std::false_type{}, std::true_type{});
+      } else {
+        step(kt, std::false_type{}, std::false_type{});
+      }
     }
     wait_vmem_all();
     __syncthreads();

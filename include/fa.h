@@ -45,7 +45,8 @@
  *             enqueues nothing.  FA_ERR_HIP reports a failed HIP launch or
  *             allocation; fa_last_error() then names it.
  *   Threads   calls hold no global mutable state apart from a per-device CU
- *             count cache and a thread-local error message; they may be made
+ *             count cache, a per-device workspace memory pool (created under
+ *             a lock) and a thread-local error message; they may be made
  *             from several threads at once.
  */
 #ifndef FA_H
@@ -94,9 +95,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * for the current device; otherwise 1 <= num_splits <= Sk.
  * Phase one writes a normalised partial output and its LSE per partition;
  * phase two merges them with log-sum-exp weights into o and lse.  Both
- * kernels run on `stream`.  The partials live in a workspace obtained with
- * hipMallocAsync on `stream` and released with hipFreeAsync on the same
- * stream after phase two (stream-ordered, so nothing blocks).
+ * kernels run on `stream`.  The partials live in a workspace taken from a
+ * per-device memory pool that the library creates on first use (stream-
+ * ordered hipMallocFromPoolAsync / hipFreeAsync on `stream`, so nothing
+ * blocks); the pool keeps freed memory for reuse until the process ends.
  */
 int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Sq, int Sk, int D, int causal, float scale,
