@@ -43,18 +43,22 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel sources."""
+def measured_traffic(kernel_keys, src_hash):
+    """HBM bytes per call (summed over the listed kernels) from the committed
+    rocprofv3 counter summary, only if it was taken on the current kernel
+    sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    entry = data.get(kernel_key)
-    if not entry or entry.get("source_hash") != src_hash:
-        return None
-    return entry.get("bytes_per_launch")
+    total = 0
+    for key in kernel_keys:
+        entry = data.get(key)
+        if not entry or entry.get("source_hash") != src_hash:
+            return None
+        total += entry["bytes_per_launch"]
+    return total
 
 
 def prefill_flops(B, H, Sq, Sk, D, causal):
@@ -129,6 +133,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library's automatic choice")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many MiB (untimed), so a "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE pass over this command can be scaled by "
+                         "what the counters read for a transfer of known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -210,7 +218,7 @@ def main():
         "peak": PEAK_FP16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-        "traffic": measured_traffic("fwd_kernel<128,64,causal>", src_hash),
+        "traffic": measured_traffic(["fwd_kernel<128,64,causal>"], src_hash),
     }
     roof_dec = {
         "kernel": "decode_partial_kernel<128> + decode_merge_kernel<128>",
@@ -219,7 +227,7 @@ def main():
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
         "frac": round(gbps / PEAK_HBM_GBPS, 4),
-        "traffic": measured_traffic("decode_partial_kernel<128>", src_hash),
+        "traffic": measured_traffic(["decode_partial_kernel<128>", "decode_merge_kernel<128>"], src_hash),
     }
     dominant, other = (roof_pre, roof_dec) if t_pre >= t_dec else (roof_dec, roof_pre)
 
@@ -252,6 +260,14 @@ def main():
         "roofline": dominant,
         "roofline_other": other,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2**20 // 2
+        x = torch.ones(n, dtype=torch.float16, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        out["config"]["copy_calibration_bytes"] = n * 2
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline((w3, *pre_host), (w4, *dec_host))
