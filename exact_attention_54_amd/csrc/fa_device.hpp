@@ -111,9 +111,17 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
 
-// Maximum / sum of x over the two 32-lane halves of a wavefront.
-__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+// Maximum / sum of x over the two 32-lane halves of a wavefront, on the
+// VALU: v_permlane32_swap(x, x) returns the low half of x in both halves
+// and the high half in both halves (pinned by a GPU probe test).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
 

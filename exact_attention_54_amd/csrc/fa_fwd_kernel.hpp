@@ -242,6 +242,40 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_nxt[kb];
     }
   };
+  // The same step for the hot part of the loop: the next tile needs no
+  // mask and S(kt+1) goes to the other register set (no copy).
+  auto step_clean = [&](int kt, f32x16 (&s_c)[C::NKB], f32x16 (&s_n)[C::NKB]) {
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    h8 pop[C::NKB][2];
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        h2 pr;
+        pr[0] = (_Float16)exp2_fast(__builtin_fmaf(s_c[kb][j], c2, -m_use));
+        pr[1] = (_Float16)exp2_fast(__builtin_fmaf(s_c[kb][j + 1], c2, -m_use));
+        l_run = dot2(pr, ones, l_run);
+        pop[kb][j >> 3][j & 7] = pr[0];
+        pop[kb][j >> 3][(j & 7) + 1] = pr[1];
+      }
+    qk((kt + 1) & 1, s_n);
+    const char* Vs = smem + C::V_BASE + (kt & 1) * C::TILE_BYTES;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int key = 32 * kb + 16 * k2 + v_key;
+          const int chunk = 4 * db + v_chunk;
+          const h4v lo = lds_read_tr16(Vs + vswz<C::KCH>(key, chunk) + v_half);
+          const h4v hi = lds_read_tr16(Vs + vswz<C::KCH>(key + 8, chunk) + v_half);
+          const h8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[db] = mfma_32x32x16(a, pop[kb][k2], oacc[db]);
+        }
+    mask_and_max(s_n, kt + 1, std::false_type{});
+  };
   auto tile_needs_mask = [&](int kt) { return (kt * BN + BN > Sk) || (CAUSAL && kt * BN + BN - 1 > qw); };
 
   // Prologue: K(0), V(0), K(1) resident, S(0) computed, masked and maxed.
@@ -257,20 +291,49 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   }
   __syncthreads();  // K stage 0 is refilled with K(2) below
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto begin_tile = [&](int kt) {
     if (kt + 2 < nkt) load_k(kt + 2, kt & 1);
     if (kt + 1 < nkt) load_v(kt + 1, (kt + 1) & 1);
+  };
+  auto rescale_if_grown = [&]() {
+    if (wave_any(grow)) {  // rare: some row max grew by more than 2^8
+      const float alpha = exp2_fast(m_run - m_cand);  // 1 where the max stays, 0 on a row's first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m_run = m_cand;
+      grow = false;
+    }
+  };
+  auto end_tile = [&]() {
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  // Hot loop, unrolled by two so the current / next S^T register sets swap
+  // roles without copies: every step kt < kclean has a next tile that this
+  // wavefront needs and that needs no mask.
+  const int kmask = min(CAUSAL ? (qw + 1) / BN : nkt_all, (Sk % BN) ? nkt_all - 1 : nkt_all);
+  const int kclean = min(kmask - 1, jlast);
+  f32x16 s_alt[C::NKB];
+  int kt = 0;
+  for (; kt + 2 <= kclean; kt += 2) {
+    begin_tile(kt);
+    rescale_if_grown();
+    step_clean(kt, s_cur, s_alt);
+    end_tile();
+    begin_tile(kt + 1);
+    rescale_if_grown();
+    step_clean(kt + 1, s_alt, s_cur);
+    end_tile();
+  }
+  // The last few tiles (diagonal, ragged tail, past this wavefront's rows).
+  for (; kt < nkt; ++kt) {
+    begin_tile(kt);
     if (kt <= jlast) {
-      if (wave_any(grow)) {  // rare: some row max grew by more than 2^8
-        const float alpha = exp2_fast(m_run - m_cand);  // 1 where the max stays, 0 on a row's first tile
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-        m_run = m_cand;
-        grow = false;
-      }
+      rescale_if_grown();
       // the mask of S(kt+1) is a compile-time variant, so unmasked tiles
       // carry no compare/select work
       if (kt + 1 < nkt) {
@@ -280,8 +343,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         step(kt, std::false_type{}, std::false_type{});
       }
     }
-    wait_vmem_all();
-    __syncthreads();
+    end_tile();
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  The O^T fragment is

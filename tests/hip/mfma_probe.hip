@@ -22,3 +22,19 @@ extern "C" int probe_mfma_32x32x16(const void* a_regs, const void* b_regs, void*
   if (hipGetLastError() != hipSuccess) return 1;
   return hipDeviceSynchronize() == hipSuccess ? 0 : 2;
 }
+
+// v_permlane32_swap with both operands = x: returns (x of lanes 0..31 in
+// both halves, x of lanes 32..63 in both halves).
+__global__ void __launch_bounds__(64) permlane_kernel(const unsigned* x, unsigned* lo, unsigned* hi) {
+  const int l = threadIdx.x;  // exactly 64 lanes, arrays hold 64 entries each
+  const auto r = __builtin_amdgcn_permlane32_swap(x[l], x[l], false, false);
+  lo[l] = r[0];
+  hi[l] = r[1];
+}
+
+extern "C" int probe_permlane32_swap(const void* x, void* lo, void* hi) {
+  hipLaunchKernelGGL(permlane_kernel, dim3(1), dim3(64), 0, 0, static_cast<const unsigned*>(x),
+                     static_cast<unsigned*>(lo), static_cast<unsigned*>(hi));
+  if (hipGetLastError() != hipSuccess) return 1;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : 2;
+}

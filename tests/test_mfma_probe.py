@@ -46,3 +46,23 @@ def test_mfma_32x32x16_layout():
         for j in range(16):
             got[8 * (j // 4) + 4 * (l // 32) + j % 4, l % 32] = c_regs[l, j]
     np.testing.assert_array_equal(got, C)
+
+
+def test_permlane32_swap_exchanges_wave_halves():
+    """xhalf_max / xhalf_sum rely on v_permlane32_swap(x, x) returning the
+    low half of x broadcast to both halves and the high half likewise."""
+    import torch
+
+    assert torch.cuda.is_available(), "GPU test needs a GPU"
+    lib = ctypes.CDLL(PROBE)
+    lib.probe_permlane32_swap.restype = ctypes.c_int
+    lib.probe_permlane32_swap.argtypes = [ctypes.c_void_p] * 3
+    dev = torch.device("cuda:0")
+    x = torch.arange(1000, 1064, dtype=torch.int32, device=dev)
+    lo = torch.zeros(64, dtype=torch.int32, device=dev)
+    hi = torch.zeros(64, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    assert lib.probe_permlane32_swap(x.data_ptr(), lo.data_ptr(), hi.data_ptr()) == 0
+    xs = list(range(1000, 1064))
+    assert lo.cpu().tolist() == xs[:32] + xs[:32]
+    assert hi.cpu().tolist() == xs[32:] + xs[32:]

@@ -121,6 +121,8 @@ RAGGED = [
     (1, 1, 1, 1),
     (1, 2, 129, 65),
     (1, 1, 257, 257),
+    (1, 2, 1000, 1000),  # long unrolled main loop with a ragged tail
+    (1, 1, 777, 1500),
 ]
 
 
