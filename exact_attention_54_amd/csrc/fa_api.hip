@@ -70,17 +70,37 @@ int hip_check(hipError_t e, const char* what) {
 
 int launched(const char* what) { return hip_check(hipGetLastError(), what); }
 
-template <int D, int BN, bool CAUSAL>
+int device_cu_count(int* out);
+
+template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
                float scale, hipStream_t stream) {
-  using Cfg = fa::FwdCfg<D, BN>;
+  using Cfg = fa::FwdCfg<D, BN, NW>;
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   const float c2 = scale * fa::kLog2e;
-  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
                      static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                      static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt, c2);
   return launched("fa_fwd kernel launch");
+}
+
+// D <= 128: 8-wavefront workgroups (256 query rows, one per CU) when that
+// still gives every CU a workgroup, else 4-wavefront ones (128 rows, two per
+// CU) so small problems spread over more CUs.
+template <int D, bool CAUSAL>
+int launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+                 float scale, hipStream_t stream) {
+  if constexpr (D == 256) {
+    return launch_fwd<256, 32, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+  } else {
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != FA_OK) return rc;
+    const int64_t wg8 = (int64_t)BH * ((Sq + 255) / 256);
+    if (wg8 >= cus) return launch_fwd<D, 64, 8, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    return launch_fwd<D, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+  }
 }
 
 template <int D>
@@ -206,14 +226,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
     case 64:
-      return causal ? launch_fwd<64, 64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd<64, 64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+      return causal ? launch_fwd_d<64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_d<64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
     case 128:
-      return causal ? launch_fwd<128, 64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd<128, 64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+      return causal ? launch_fwd_d<128, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_d<128, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
     default:
-      return causal ? launch_fwd<256, 32, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd<256, 32, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+      return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
   }
 }
 

@@ -1,6 +1,6 @@
 // Exact attention forward (prefill) for gfx950, FlashAttention-2 loop order.
 //
-// One workgroup = 4 wavefronts = BM = 128 query rows ("Split-Q"; the loop
+// One workgroup = NW wavefronts = BM = 32*NW query rows ("Split-Q"; the loop
 // inversion of "Adaptive High-Performance Attention Kernels in CUDA",
 // Architectural Progression, Stage 3: outer query tile, inner key/value
 // stream, output accumulator in registers).  Each wavefront owns 32 query
@@ -44,9 +44,9 @@
 
 namespace fa {
 
-template <int D, int BN>
+template <int D, int BN, int NW>
 struct FwdCfg {
-  static constexpr int NWAVES = 4;
+  static constexpr int NWAVES = NW;
   static constexpr int THREADS = 64 * NWAVES;
   static constexpr int BM = 32 * NWAVES;
   static constexpr int KCH = D / 8;    // 16-byte chunks per K / V row
@@ -66,18 +66,21 @@ struct FwdCfg {
 // Row-max growth (log2 units) tolerated before the reference max moves.
 constexpr float kLazyRescale = 8.0f;
 
-// Workgroups per CU the register budget is sized for: two at D <= 128, so
-// one workgroup's softmax overlaps the other's MFMAs; one at D = 256, whose
-// 32 x 256 fp32 accumulator per wavefront needs the whole register file.
-template <int D>
-constexpr int fwd_wg_per_cu() { return D <= 128 ? 2 : 1; }
+// Workgroups per CU the register budget is sized for.  Two wavefronts per
+// SIMD let one wavefront's softmax overlap the other's MFMAs: at D <= 128
+// that is one 8-wavefront workgroup (every K/V tile in LDS then serves 256
+// query rows) or two 4-wavefront ones (twice the workgroups, for small
+// grids).  At D = 256 the 32 x 256 fp32 accumulator of a wavefront needs the
+// whole register file: one 4-wavefront workgroup.
+template <int D, int NW>
+constexpr int fwd_wg_per_cu() { return (D <= 128 && NW == 4) ? 2 : 1; }
 
-template <int D, int BN, bool CAUSAL>
-__global__ void __launch_bounds__(256, fwd_wg_per_cu<D>())
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<D, NW>()))
 fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
            const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
            int Sq, int Sk, int BH, int nqt, float c2) {
-  using C = FwdCfg<D, BN>;
+  using C = FwdCfg<D, BN, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;

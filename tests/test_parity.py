@@ -138,6 +138,26 @@ def test_ragged_prefill(torch_dev, fa, D, shape, causal):
     assert_close(o, lse, O, L, f"D={D} {shape} causal={causal}")
 
 
+WIDE = [
+    # B*H = 256 slices: enough workgroups that D <= 128 runs 8-wavefront workgroups
+    (4, 64, 300, 333),
+    (2, 128, 257, 1000),
+    (1, 256, 1, 700),
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("shape", WIDE, ids=["x".join(map(str, s)) for s in WIDE])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_grid_prefill(torch_dev, fa, D, shape, causal):
+    B, H, Sq, Sk = shape
+    q, k, v = make_qkv(B, H, Sq, Sk, D, seed=2000 + Sq + Sk + D)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = gpu_fwd(torch_dev, fa, q, k, v, causal, scale)
+    O, L = oracle.attention(q, k, v, causal, scale)
+    assert_close(o, lse, O, L, f"wide D={D} {shape} causal={causal}")
+
+
 @pytest.mark.parametrize("scale", [0.05, 0.3, 1.0])
 def test_other_scales_and_large_scores(torch_dev, fa, scale):
     q, k, v = make_qkv(1, 2, 160, 160, 128, seed=77)
