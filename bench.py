@@ -5,6 +5,8 @@ One step = the whole path once over one batch of synthetic fp16 N(0,1) input:
     (B, H, Sq, Sk, D) = (1, 32, 4096, 4096, 128), scale 1/sqrt(128);
   * split-KV decoding fa_decode_splitkv on (16, 32, 1, 8192, 128),
     num_splits chosen by the library to fill the CUs.
+After the timed steps, paged decoding (fa_decode_paged) of the same K / V in
+16-token pages is timed on its own and reported beside the step figures.
 Inputs are resident in HBM before the timed region.  Prefill throughput
 counts 4*B*H*Sq*Sk*D FLOPs halved for the causal mask; decode throughput
 counts the bytes of K and V read.  rank 0 prints one JSON line on stdout;
@@ -139,15 +141,15 @@ def main():
                          "what the counters read for a transfer of known size")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the path shards over heads/keys with no collectives, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the prefill "
+              "shards over heads and the decode over keys, and no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
     import torch
 
     import exact_attention_54_amd as fa
-    from workloads import WORKLOADS, workload_inputs
+    from workloads import PAGED_BLOCK_SIZE, PAGED_PERM_SEED, WORKLOADS, paged_layout, workload_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -210,6 +212,31 @@ def main():
     t_pre_hot = time_launches(torch, prefill, args.steps)
     log(f"prefill back-to-back (K/V cache-warm): {t_pre_hot * 1e6:.1f} us = {flops / t_pre_hot / 1e12:.1f} TFLOPS")
 
+    # Paged decoding of the same K / V, held in 16-token pages in a seeded
+    # random physical order (built on the GPU, untimed); timed back to back.
+    bs = PAGED_BLOCK_SIZE
+    max_blocks = w4.Sk // bs
+    tables, nb = paged_layout(w4.B, max_blocks, PAGED_PERM_SEED)
+    td = torch.from_numpy(tables).to(dev)
+    idx = td.reshape(-1).long()
+    kc = torch.empty((nb, w4.H, bs, w4.D), dtype=torch.float16, device=dev)
+    vc = torch.empty_like(kc)
+    kc[idx] = k4.view(w4.B, w4.H, max_blocks, bs, w4.D).permute(0, 2, 1, 3, 4).reshape(-1, w4.H, bs, w4.D)
+    vc[idx] = v4.view(w4.B, w4.H, max_blocks, bs, w4.D).permute(0, 2, 1, 3, 4).reshape(-1, w4.H, bs, w4.D)
+    sl = torch.full((w4.B,), w4.Sk, dtype=torch.int32, device=dev)
+    op4 = torch.empty_like(o4)
+    lp4 = torch.empty_like(l4)
+
+    def paged():
+        fa.fa_decode_paged(q4, kc, vc, td, sl, op4, lp4, scale=w4.scale, num_splits=ns)
+
+    for _ in range(args.warmup):
+        paged()
+    t_paged = time_launches(torch, paged, args.steps)
+    gbps_paged = kv_bytes / t_paged / 1e9
+    log(f"paged decode (block_size {bs}, random page order): {t_paged * 1e6:.1f} us = {gbps_paged:.1f} GB/s")
+    del kc, vc
+
     src_hash = kernel_source_hash()
     roof_pre = {
         "kernel": "fwd_kernel<128,64,causal>",
@@ -254,6 +281,10 @@ def main():
             "prefill_us": round(t_pre * 1e6, 2),
             "decode_us": round(t_dec * 1e6, 2),
             "prefill_us_back_to_back": round(t_pre_hot * 1e6, 2),
+            "paged_decode_gbps": round(gbps_paged, 2),
+            "paged_decode_frac_of_peak": round(gbps_paged / PEAK_HBM_GBPS, 4),
+            "paged_decode_us": round(t_paged * 1e6, 2),
+            "paged_block_size": bs,
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,
         },

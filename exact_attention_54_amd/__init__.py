@@ -7,6 +7,7 @@ library is missing or the tensors are not on a GPU, the call raises.
 
     o, lse = fa_fwd(q, k, v, causal=True)                  # q,k,v fp16 [B,H,S,D]
     o, lse = fa_decode_splitkv(q, k, v, num_splits=0)      # Sq == 1, 0 = auto
+    o, lse = fa_decode_paged(q, k_cache, v_cache, block_tables, seq_lens)
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ __all__ = [
     "fa_fwd",
     "fa_decode_splitkv",
     "fa_decode_splitkv_ws",
+    "fa_decode_paged",
     "fa_decode_workspace_bytes",
     "fa_decode_auto_splits",
     "fa_status_string",
@@ -120,6 +122,43 @@ def fa_decode_splitkv_ws(q, k, v, workspace, o=None, lse=None, causal=False, sca
                                   B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream),
                                   int(num_splits), workspace.data_ptr(), nbytes)
     _capi.check(st, "fa_decode_splitkv_ws")
+    return o, lse
+
+
+def fa_decode_paged(q, k_cache, v_cache, block_tables, seq_lens, o=None, lse=None, scale=None, stream=None,
+                    num_splits=0):
+    """Split-KV decoding over a paged KV cache; returns (o, lse).  See fa_decode_paged in include/fa.h.
+
+    q fp16 [B, H, 1, D]; k_cache / v_cache fp16 [num_blocks, H, block_size, D];
+    block_tables int32 [B, max_blocks]; seq_lens int32 [B] (all on q's device).
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float16 torch.Tensor on a GPU")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 torch.Tensor")
+    for t in (k_cache, v_cache, block_tables, seq_lens):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on q's device")
+    B, H, Sq, D = q.shape
+    num_blocks, Hc, block_size, Dc = k_cache.shape
+    if Sq != 1 or Hc != H or Dc != D or v_cache.shape != k_cache.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k_cache {tuple(k_cache.shape)} "
+                         f"v_cache {tuple(v_cache.shape)}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
+    o, lse = _outputs(q, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _capi.load()
+    st = lib.fa_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                             seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, D, num_blocks, block_size,
+                             block_tables.shape[1], float(scale), _stream(q, stream), int(num_splits))
+    _capi.check(st, "fa_decode_paged")
     return o, lse
 
 

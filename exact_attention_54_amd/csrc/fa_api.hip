@@ -118,6 +118,23 @@ int launch_decode(const void* q, const void* k, const void* v, void* o, float* l
   return launched("decode merge launch");
 }
 
+template <int D>
+int launch_decode_paged(const void* q, const void* kc, const void* vc, const int* tables, const int* seq_lens,
+                        void* o, float* lse, int B, int H, int num_blocks, int lbs, int max_blocks, float scale,
+                        hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
+  const float c2 = scale * fa::kLog2e;
+  const int BH = B * H;
+  hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D>), dim3(BH * ns), dim3(fa::DecCfg<D>::THREADS), 0,
+                     stream, static_cast<const _Float16*>(q), static_cast<const _Float16*>(kc),
+                     static_cast<const _Float16*>(vc), tables, seq_lens, ws_o, ws_lse, H, ns, num_blocks, lbs,
+                     max_blocks, c2);
+  int rc = launched("paged decode phase-one launch");
+  if (rc != FA_OK) return rc;
+  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
+                     static_cast<_Float16*>(o), lse, ns);
+  return launched("paged decode merge launch");
+}
+
 std::atomic<int> g_cu_count[64];
 
 int device_cu_count(int* out) {
@@ -163,7 +180,7 @@ int workspace_pool(hipMemPool_t* out) {
     uint64_t keep = UINT64_MAX;
     rc = hip_check(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep), "pool release threshold");
     if (rc != FA_OK) {
-      hipMemPoolDestroy(pool);
+      (void)hipMemPoolDestroy(pool);
       return rc;
     }
     g_pool[dev] = pool;
@@ -197,6 +214,34 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
     case 128: return launch_decode<128>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
     default: return launch_decode<256>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
   }
+}
+
+int validate_paged(const void* q, const void* kc, const void* vc, const int* tables, const int* seq_lens,
+                   const void* o, const void* lse, int B, int H, int D, int num_blocks, int block_size,
+                   int max_blocks, float scale, int num_splits, int* lbs) {
+  if (!q || !kc || !vc || !tables || !seq_lens || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || H < 1 || D < 1 || num_blocks < 1 || max_blocks < 1)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d D=%d num_blocks=%d max_blocks=%d)", B, H, D,
+                num_blocks, max_blocks);
+  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
+    return fail(FA_ERR_INVALID_ARG, "block_size %d is not a power of two in [1, 1024]", block_size);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(tables, 4) || !aligned(seq_lens, 4))
+    return fail(FA_ERR_INVALID_ARG, "lse, block_tables and seq_lens must be 4-byte aligned");
+  const int64_t max_ctx = (int64_t)max_blocks * block_size;
+  if (max_ctx >= (int64_t(1) << 30)) return fail(FA_ERR_INVALID_ARG, "max_blocks * block_size too large");
+  if (!product_le(num_blocks, H, block_size, D, kMaxElems)) return fail(FA_ERR_INVALID_ARG, "cache too large");
+  if (!product_le(B, max_blocks, 1, 1, kMaxElems)) return fail(FA_ERR_INVALID_ARG, "block table too large");
+  if (num_splits > max_ctx) return fail(FA_ERR_INVALID_ARG, "num_splits %d exceeds max context %lld", num_splits,
+                                        (long long)max_ctx);
+  if ((int64_t)B * H * (num_splits > 0 ? num_splits : 1) > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  int l = 0;
+  while ((1 << l) < block_size) ++l;
+  *lbs = l;
+  return FA_OK;
 }
 
 int resolve_splits(int B, int H, int Sk, int num_splits, int* ns) {
@@ -284,6 +329,43 @@ int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, floa
   rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)B * H, D, ns), pool, s), "workspace allocation");
   if (rc != FA_OK) return rc;
   rc = run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, ns, ws);
+  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
+  return rc != FA_OK ? rc : frc;
+}
+
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,
+                    const int* seq_lens, void* o, float* lse, int B, int H, int D, int num_blocks, int block_size,
+                    int max_blocks, float scale, void* stream, int num_splits) {
+  int lbs = 0;
+  int rc = validate_paged(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, D, num_blocks, block_size,
+                          max_blocks, scale, num_splits, &lbs);
+  if (rc != FA_OK) return rc;
+  int ns = 0;
+  rc = resolve_splits(B, H, max_blocks * block_size, num_splits, &ns);
+  if (rc != FA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipMemPool_t pool = nullptr;
+  rc = workspace_pool(&pool);
+  if (rc != FA_OK) return rc;
+  void* ws = nullptr;
+  rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)B * H, D, ns), pool, s), "workspace allocation");
+  if (rc != FA_OK) return rc;
+  float* ws_o = static_cast<float*>(ws);
+  float* ws_lse = ws_o + (size_t)B * H * ns * D;
+  switch (D) {
+    case 64:
+      rc = launch_decode_paged<64>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
+                                   max_blocks, scale, s, ns, ws_o, ws_lse);
+      break;
+    case 128:
+      rc = launch_decode_paged<128>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
+                                    max_blocks, scale, s, ns, ws_o, ws_lse);
+      break;
+    default:
+      rc = launch_decode_paged<256>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
+                                    max_blocks, scale, s, ns, ws_o, ws_lse);
+      break;
+  }
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
 }

@@ -34,65 +34,33 @@ struct DecCfg {
   static constexpr int NSTATE = NWAVES * SLOTS;          // independent softmax states per workgroup
 };
 
-// ws_o: [BH, ns, D] fp32, ws_lse: [BH, ns] fp32 (natural log).
-template <int D>
-__global__ void __launch_bounds__(256)
-decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-                      const _Float16* __restrict__ V, float* __restrict__ ws_o,
-                      float* __restrict__ ws_lse, int Sk, int ns, int chunk, float c2) {
+// Online softmax of one lane slot over the keys [kb, ke) that this
+// wavefront visits (keys base + u * SLOTS + slot, base stepping by the
+// workgroup's stride).  row_of(key) is the element offset of the key's K and
+// V rows, or -1 for a key that is absent (it then scores -inf).
+template <int D, class RowOf>
+__device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::CPL][8],
+                                                  const _Float16* __restrict__ kp,
+                                                  const _Float16* __restrict__ vp, int kb, int ke,
+                                                  RowOf row_of, int w, int slot, int dl, float c2,
+                                                  float& m_run, float& l_run,
+                                                  float (&acc)[DecCfg<D>::CPL][8]) {
   using C = DecCfg<D>;
-  __shared__ float s_m[C::NSTATE];
-  __shared__ float s_l[C::NSTATE];
-  __shared__ __attribute__((aligned(16))) float s_acc[C::NSTATE][D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int slot = lane / C::LPK;
-  const int dl = lane % C::LPK;
-  const int bh = blockIdx.x / ns;
-  const int s = blockIdx.x - bh * ns;
-  const int k0 = s * chunk;
-  const int k1 = min(Sk, k0 + chunk);
-  float* out_o = ws_o + ((size_t)bh * ns + s) * D;
-
-  if (k0 >= k1) {  // empty partition: weight zero in the merge
-    for (int d = tid; d < D; d += C::THREADS) out_o[d] = 0.f;
-    if (tid == 0) ws_lse[(size_t)bh * ns + s] = kNegInf;
-    return;
-  }
-
-  const _Float16* qp = Q + (size_t)bh * D;
-  const _Float16* kp = K + (size_t)bh * Sk * D;
-  const _Float16* vp = V + (size_t)bh * Sk * D;
-
-  float qf[C::CPL][8];
-#pragma unroll
-  for (int c = 0; c < C::CPL; ++c) {
-    const h8 t = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[c][e] = (float)t[e];
-  }
-
-  float m_run = kNegInf, l_run = 0.f;
-  float acc[C::CPL][8];
-#pragma unroll
-  for (int c = 0; c < C::CPL; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-
-  for (int base = k0 + w * C::KEYS_PER_WAVE_ITER; base < k1; base += C::KEYS_PER_WG_ITER) {
+  for (int base = kb + w * C::KEYS_PER_WAVE_ITER; base < ke; base += C::KEYS_PER_WG_ITER) {
     u32x4 kr[C::U][C::CPL], vr[C::U][C::CPL];
+    bool present[C::U];
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       const int key = base + u * C::SLOTS + slot;
+      const int64_t row = (key < ke) ? row_of(key) : -1;
+      present[u] = row >= 0;
 #pragma unroll
       for (int c = 0; c < C::CPL; ++c) {
         u32x4 tk = {0u, 0u, 0u, 0u}, tv = {0u, 0u, 0u, 0u};
-        if (key < k1) {
+        if (present[u]) {
           // read once: non-temporal loads keep the stream from evicting
           // useful cache lines (measured ~13% more HBM bandwidth)
-          const size_t off = (size_t)key * D + (dl + c * C::LPK) * 8;
+          const size_t off = (size_t)row * D + (dl + c * C::LPK) * 8;
           tk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
           tv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
         }
@@ -112,8 +80,7 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
       }
 #pragma unroll
       for (int off = 1; off < C::LPK; off <<= 1) part += __shfl_xor(part, off);
-      const int key = base + u * C::SLOTS + slot;
-      sc[u] = (key < k1) ? part : kNegInf;
+      sc[u] = present[u] ? part : kNegInf;
     }
     float mx = sc[0];
 #pragma unroll
@@ -139,8 +106,19 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
     }
     m_run = m_new;
   }
+}
 
-  // Merge the NSTATE slot states of this workgroup.
+// Merges the NSTATE slot states of a workgroup through LDS into the
+// normalised partial output out_o[0..D) and its natural-log lse.  A
+// partition whose slots saw no present key gets O_s = 0, lse_s = -inf.
+template <int D>
+__device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, const float (&acc)[DecCfg<D>::CPL][8],
+                                                   int tid, int w, int slot, int dl, float* __restrict__ out_o,
+                                                   float* __restrict__ out_lse) {
+  using C = DecCfg<D>;
+  __shared__ float s_m[C::NSTATE];
+  __shared__ float s_l[C::NSTATE];
+  __shared__ __attribute__((aligned(16))) float s_acc[C::NSTATE][D];
   const int st = w * C::SLOTS + slot;
   if (dl == 0) {
     s_m[st] = m_run;
@@ -156,6 +134,11 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 #pragma unroll
   for (int i = 0; i < C::NSTATE; ++i) M = fmaxf(M, s_m[i]);
   for (int d = tid; d < D; d += C::THREADS) {
+    if (M == kNegInf) {  // no present key in the partition
+      out_o[d] = 0.f;
+      if (d == 0) *out_lse = kNegInf;
+      continue;
+    }
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int i = 0; i < C::NSTATE; ++i) {
@@ -164,8 +147,133 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
       num += wgt * s_acc[i][d];
     }
     out_o[d] = num / den;
-    if (d == 0) ws_lse[(size_t)bh * ns + s] = (M + __builtin_log2f(den)) * kLn2;
+    if (d == 0) *out_lse = (M + __builtin_log2f(den)) * kLn2;
   }
+}
+
+// ws_o: [BH, ns, D] fp32, ws_lse: [BH, ns] fp32 (natural log).
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                      const _Float16* __restrict__ V, float* __restrict__ ws_o,
+                      float* __restrict__ ws_lse, int Sk, int ns, int chunk, float c2) {
+  using C = DecCfg<D>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int slot = lane / C::LPK;
+  const int dl = lane % C::LPK;
+  const int bh = blockIdx.x / ns;
+  const int s = blockIdx.x - bh * ns;
+  const int k0 = s * chunk;
+  const int k1 = min(Sk, k0 + chunk);
+  float* out_o = ws_o + ((size_t)bh * ns + s) * D;
+
+  if (k0 >= k1) {  // empty partition: weight zero in the merge
+    for (int d = tid; d < D; d += C::THREADS) out_o[d] = 0.f;
+    if (tid == 0) ws_lse[(size_t)bh * ns + s] = kNegInf;
+    return;
+  }
+
+  const _Float16* qp = Q + (size_t)bh * D;
+  float qf[C::CPL][8];
+#pragma unroll
+  for (int c = 0; c < C::CPL; ++c) {
+    const h8 t = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[c][e] = (float)t[e];
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[C::CPL][8];
+#pragma unroll
+  for (int c = 0; c < C::CPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+
+  decode_accumulate<D>(qf, K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, k0, k1,
+                       [](int key) { return (int64_t)key; }, w, slot, dl, c2, m_run, l_run, acc);
+  decode_merge_slots<D>(m_run, l_run, acc, tid, w, slot, dl, out_o, ws_lse + (size_t)bh * ns + s);
+}
+
+// Paged KV cache ("Adaptive High-Performance Attention Kernels in CUDA",
+// Advanced Production Features, 4. PagedAttention): K and V live in
+// fixed-size physical blocks [num_blocks, H, block_size, D], and row b of
+// the block table [B, max_blocks] names the physical block that holds
+// logical block j (keys j*block_size .. +block_size-1) of sequence b.  The
+// workgroup of (b, h, partition) copies the table entries of its key range
+// to LDS (in segments of at most kPagedTbl blocks), then streams keys as the
+// contiguous kernel does, translating each key to its physical row.  Table
+// entries outside [0, num_blocks) mark absent keys: they are never read.
+constexpr int kPagedTbl = 1024;
+
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ Kc,
+                            const _Float16* __restrict__ Vc, const int* __restrict__ tables,
+                            const int* __restrict__ seq_lens, float* __restrict__ ws_o,
+                            float* __restrict__ ws_lse, int H, int ns, int num_blocks, int lbs,
+                            int max_blocks, float c2) {
+  using C = DecCfg<D>;
+  __shared__ int s_tbl[kPagedTbl];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int slot = lane / C::LPK;
+  const int dl = lane % C::LPK;
+  const int bh = blockIdx.x / ns;
+  const int s = blockIdx.x - bh * ns;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  // context length, clamped to what the table row can address
+  const int L = min(max(seq_lens[b], 0), max_blocks << lbs);
+  const int chunk = (L + ns - 1) / ns;
+  const int k0 = s * chunk;
+  const int k1 = min(L, k0 + chunk);
+  float* out_o = ws_o + ((size_t)bh * ns + s) * D;
+
+  if (k0 >= k1) {  // empty partition (or empty context): weight zero in the merge
+    for (int d = tid; d < D; d += C::THREADS) out_o[d] = 0.f;
+    if (tid == 0) ws_lse[(size_t)bh * ns + s] = kNegInf;
+    return;
+  }
+
+  const _Float16* qp = Q + (size_t)bh * D;
+  float qf[C::CPL][8];
+#pragma unroll
+  for (int c = 0; c < C::CPL; ++c) {
+    const h8 t = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[c][e] = (float)t[e];
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[C::CPL][8];
+#pragma unroll
+  for (int c = 0; c < C::CPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+
+  const int* trow = tables + (size_t)b * max_blocks;
+  const int bmask = (1 << lbs) - 1;
+  const int seg_keys = (kPagedTbl - 1) << lbs;  // a segment spans at most kPagedTbl blocks
+  for (int seg = k0; seg < k1; seg += seg_keys) {
+    const int seg_end = min(k1, seg + seg_keys);
+    const int blk0 = seg >> lbs;
+    const int nblk = ((seg_end - 1) >> lbs) - blk0 + 1;
+    __syncthreads();  // the previous segment's table reads are done
+    for (int i = tid; i < nblk; i += C::THREADS) s_tbl[i] = trow[blk0 + i];
+    __syncthreads();
+    decode_accumulate<D>(
+        qf, Kc, Vc, seg, seg_end,
+        [&](int key) -> int64_t {
+          const int pb = s_tbl[(key >> lbs) - blk0];
+          if ((unsigned)pb >= (unsigned)num_blocks) return -1;
+          return (((int64_t)pb * H + h) << lbs) + (key & bmask);
+        },
+        w, slot, dl, c2, m_run, l_run, acc);
+  }
+  decode_merge_slots<D>(m_run, l_run, acc, tid, w, slot, dl, out_o, ws_lse + (size_t)bh * ns + s);
 }
 
 template <int D>
@@ -178,6 +286,11 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   float M = kNegInf;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, lp[s]);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    if (M == kNegInf) {  // no key at all (empty paged context): O = 0, LSE = -inf
+      O[(size_t)bh * D + d] = (_Float16)0.f;
+      if (d == 0) LSE[bh] = kNegInf;
+      continue;
+    }
     float den = 0.f, num = 0.f;
     for (int s = 0; s < ns; ++s) {
       const float wgt = exp2_fast((lp[s] - M) * kLog2e);

@@ -126,6 +126,37 @@ int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, f
                          void* stream, int num_splits, void* workspace, size_t workspace_bytes);
 
 /*
+ * fa_decode_paged -- fa_decode_splitkv over a paged KV cache ("Adaptive
+ * High-Performance Attention Kernels in CUDA", Advanced Production
+ * Features, 4. PagedAttention: physical pages [num_blocks, H, block_size, D]
+ * and a block table translating logical token positions to pages).
+ *
+ *   q, o          fp16 [B, H, 1, D]; lse fp32 [B, H, 1] (16- / 4-byte aligned)
+ *   k_cache,      fp16 [num_blocks, H, block_size, D], 16-byte aligned
+ *   v_cache
+ *   block_tables  int32 [B, max_blocks] device memory: entry (b, j) is the
+ *                 physical block holding keys j*block_size .. +block_size-1
+ *                 of sequence b (4-byte aligned)
+ *   seq_lens      int32 [B] device memory: context length of each sequence
+ *   block_size    a power of two, 1 .. 1024
+ * Sequence b attends, non-causally, to its keys 0 .. seq_lens[b]-1, split
+ * into num_splits partitions of ceil(seq_lens[b] / num_splits) keys as in
+ * fa_decode_splitkv.  Device-side values are not trusted: seq_lens[b] is
+ * clamped to [0, max_blocks * block_size], a table entry outside
+ * [0, num_blocks) marks its keys absent (they are never read and do not
+ * count), and a sequence with no present key gets o = 0 and lse = -inf.
+ * num_splits <= 0 picks fa_decode_auto_splits(B, H, max_blocks *
+ * block_size, CUs); otherwise 1 <= num_splits <= max_blocks * block_size.
+ * Workspace, pool and stream behaviour as fa_decode_splitkv.  Returns
+ * FA_ERR_INVALID_ARG for null / misaligned pointers or bad sizes,
+ * FA_ERR_UNSUPPORTED for D not in {64, 128, 256}.
+ */
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                    const int* block_tables, const int* seq_lens, void* o, float* lse,
+                    int B, int H, int D, int num_blocks, int block_size, int max_blocks,
+                    float scale, void* stream, int num_splits);
+
+/*
  * fa_decode_auto_splits -- the split count fa_decode_splitkv uses when
  * num_splits <= 0: the smallest power of two that gives at least
  * 8 * num_cus phase-one workgroups, lowered until every partition holds at

@@ -12,9 +12,13 @@ Contents
   dense.split_partials    per-chunk partial results of split-KV decoding
   dense.merge_partials    the log-sum-exp merge of those partials
   dense.decode_splitkv    split-KV decoding = merge(split(...))
+  paged.decode_paged      single-query decoding over a paged KV cache (block tables)
+  paged.gather_context    the present context rows of one sequence, in token order
   brute.attention_brute   pure-Python scalar loops, for tiny inputs only
+  brute.decode_paged_brute  paged decoding with scalar loops and explicit table lookups
 
-Every function is pinned by tests in ``tests/test_oracle.py`` against
+Every function is pinned by tests in ``tests/test_oracle.py`` and
+``tests/test_oracle_paged.py`` against
 closed forms, hand-derived worked examples (``tests/golden/``), invariants of
 the definition, brute force and ``torch.nn.functional.scaled_dot_product_attention``
 in fp64 on the CPU.  No function here is "parity unpinned".
@@ -28,7 +32,8 @@ from .dense import (
     split_partials,
     split_bounds,
 )
-from .brute import attention_brute
+from .brute import attention_brute, decode_paged_brute
+from .paged import decode_paged, gather_context
 
 __all__ = [
     "attention",
@@ -39,4 +44,7 @@ __all__ = [
     "split_partials",
     "split_bounds",
     "attention_brute",
+    "decode_paged",
+    "gather_context",
+    "decode_paged_brute",
 ]

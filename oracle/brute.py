@@ -53,3 +53,49 @@ def attention_brute(q, k, v, causal, scale):
         O_all.append(O_b)
         L_all.append(L_b)
     return O_all, L_all
+
+
+def decode_paged_brute(q, k_cache, v_cache, block_tables, seq_lens, scale):
+    """Paged single-query decoding with scalar loops: token t of sequence b is
+    read from page block_tables[b][t // block_size], row t % block_size; pages
+    outside [0, num_blocks) are skipped, the context is clamped to the table's
+    reach, and an empty context gives O = 0, LSE = -inf (the readings listed
+    in ``paged.py``).  Returns nested lists [B][H][1][D] and [B][H][1]."""
+    num_blocks = len(k_cache)
+    block_size = len(k_cache[0][0])
+    O_all, L_all = [], []
+    for b in range(len(q)):
+        reach = len(block_tables[b]) * block_size
+        ctx = min(max(int(seq_lens[b]), 0), reach)
+        O_b, L_b = [], []
+        for h in range(len(q[b])):
+            qv = q[b][h][0]
+            scores = []
+            for t in range(ctx):
+                page = int(block_tables[b][t // block_size])
+                if page < 0 or page >= num_blocks:
+                    continue
+                krow = k_cache[page][h][t % block_size]
+                dot = 0.0
+                for d in range(len(qv)):
+                    dot += float(qv[d]) * float(krow[d])
+                scores.append((page, t % block_size, scale * dot))
+            Dv = len(v_cache[0][0][0])
+            if not scores:
+                O_b.append([[0.0] * Dv])
+                L_b.append([-math.inf])
+                continue
+            mx = max(s for _, _, s in scores)
+            den = 0.0
+            row = [0.0] * Dv
+            for page, r, s in scores:
+                e = math.exp(s - mx)
+                den += e
+                vrow = v_cache[page][h][r]
+                for d in range(Dv):
+                    row[d] += e * float(vrow[d])
+            O_b.append([[x / den for x in row]])
+            L_b.append([mx + math.log(den)])
+        O_all.append(O_b)
+        L_all.append(L_b)
+    return O_all, L_all

@@ -12,6 +12,15 @@ Recipe (the same everywhere):
   * each value is rounded to IEEE fp16 (round-to-nearest-even).
 The causal and non-causal runs of one workload reuse the same tensors.
 
+Paged KV caches (for paged decoding) are laid out from the same contiguous
+K / V draws: every sequence's context is cut into logical blocks of
+block_size tokens, and the logical blocks of all sequences are dealt to
+physical pages [num_blocks, H, block_size, D] in a seeded random order
+(``paged_layout`` / ``to_pages``), so that consecutive blocks of one sequence
+are scattered through the cache as they would be after many allocations and
+frees.  Pages that no table entry names are filled with NaN, so a read of one
+would show up in the result.
+
 The shapes follow the pages' workloads: the LLaMA-7B prefill shape
 (1, 32, 4096, 4096, 128) and the 8K-context single-query decode shape of the
 "FlashAttention-2 MMA" benchmark tables, the B8/H16/S256/D64 shape of
@@ -75,6 +84,33 @@ def make_qkv(B: int, H: int, Sq: int, Sk: int, D: int, seed: int):
 
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.Sq, w.Sk, w.D, w.seed)
+
+
+# Paged decoding: the 8K decode shape with its K / V held in 16-token pages.
+PAGED_BLOCK_SIZE = 16
+PAGED_PERM_SEED = 6
+
+
+def paged_layout(B: int, max_blocks: int, seed: int, spare: int = 0):
+    """Block tables [B, max_blocks] int32 naming distinct physical pages in a
+    seeded random order, plus the page count (B * max_blocks + spare)."""
+    num_blocks = B * max_blocks + spare
+    gen = np.random.Generator(np.random.PCG64(seed))
+    perm = gen.permutation(num_blocks)[: B * max_blocks]
+    return perm.reshape(B, max_blocks).astype(np.int32), num_blocks
+
+
+def to_pages(x: np.ndarray, tables: np.ndarray, num_blocks: int, block_size: int) -> np.ndarray:
+    """Scatter contiguous [B, H, S, D] rows into pages [num_blocks, H, block_size, D]:
+    rows j*block_size .. of sequence b go to page tables[b, j].  S may be shorter
+    than the tables' reach (the rest of those pages stays NaN), unnamed pages are NaN."""
+    B, H, S, D = x.shape
+    pages = np.full((num_blocks, H, block_size, D), np.nan, dtype=x.dtype)
+    for b in range(B):
+        for j in range(-(-S // block_size)):
+            lo, hi = j * block_size, min(S, (j + 1) * block_size)
+            pages[tables[b, j], :, : hi - lo, :] = x[b, :, lo:hi, :]
+    return pages
 
 
 def sample_rows(w: Workload, count: int, seed: int = 12345):
