@@ -6,7 +6,10 @@ One step = the whole path once over one batch of synthetic fp16 N(0,1) input:
   * split-KV decoding fa_decode_splitkv on (16, 32, 1, 8192, 128),
     num_splits chosen by the library to fill the CUs.
 After the timed steps, paged decoding (fa_decode_paged) of the same K / V in
-16-token pages is timed on its own and reported beside the step figures.
+16-token pages, and packed variable-length causal prefill (fa_fwd_varlen) of
+16 sequences of 256..4096 tokens (with the same batch zero-padded through
+fa_fwd for comparison), are timed on their own and reported beside the step
+figures.
 Inputs are resident in HBM before the timed region.  Prefill throughput
 counts 4*B*H*Sq*Sk*D FLOPs halved for the causal mask; decode throughput
 counts the bytes of K and V read.  rank 0 prints one JSON line on stdout;
@@ -149,7 +152,9 @@ def main():
     import torch
 
     import exact_attention_54_amd as fa
-    from workloads import PAGED_BLOCK_SIZE, PAGED_PERM_SEED, WORKLOADS, paged_layout, workload_inputs
+    from workloads import (PAGED_BLOCK_SIZE, PAGED_PERM_SEED, VARLEN_B, VARLEN_D, VARLEN_H, VARLEN_LEN_SEED,
+                           VARLEN_MAX, VARLEN_MIN, VARLEN_SEED, WORKLOADS, make_varlen, paged_layout,
+                           varlen_lengths, workload_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -237,6 +242,42 @@ def main():
     log(f"paged decode (block_size {bs}, random page order): {t_paged * 1e6:.1f} us = {gbps_paged:.1f} GB/s")
     del kc, vc
 
+    # Packed variable-length causal prefill: 16 sequences of 256..4096 tokens
+    # (LLaMA-7B heads), timed back to back, and the same batch zero-padded to
+    # its longest sequence through fa_fwd, the padding the packed layout avoids.
+    lens = varlen_lengths(VARLEN_B, VARLEN_MIN, VARLEN_MAX, VARLEN_LEN_SEED)
+    vq, vk, vv, cu_q, cu_k = make_varlen(lens, VARLEN_H, VARLEN_D, VARLEN_SEED)
+    vq, vk, vv, cqd, ckd = (torch.from_numpy(x).to(dev) for x in (vq, vk, vv, cu_q, cu_k))
+    vo = torch.empty_like(vq)
+    vl = torch.empty((VARLEN_H, vq.shape[0]), dtype=torch.float32, device=dev)
+    Lmax = int(lens.max())
+    vscale = VARLEN_D ** -0.5
+
+    def varlen():
+        fa.fa_fwd_varlen(vq, vk, vv, cqd, ckd, Lmax, Lmax, vo, vl, causal=True, scale=vscale)
+
+    pads = [torch.zeros((VARLEN_B, VARLEN_H, Lmax, VARLEN_D), dtype=torch.float16, device=dev) for _ in range(3)]
+    for b in range(VARLEN_B):
+        s0, n = int(cu_q[b]), int(lens[b])
+        for dst, src in zip(pads, (vq, vk, vv)):
+            dst[b, :, :n] = src[s0:s0 + n].permute(1, 0, 2)
+    po = torch.empty_like(pads[0])
+    pl = torch.empty((VARLEN_B, VARLEN_H, Lmax), dtype=torch.float32, device=dev)
+
+    def padded():
+        fa.fa_fwd(pads[0], pads[1], pads[2], po, pl, causal=True, scale=vscale)
+
+    for _ in range(args.warmup):
+        varlen()
+        padded()
+    t_var = time_launches(torch, varlen, args.steps)
+    t_pad = time_launches(torch, padded, args.steps)
+    flops_var = float(sum(4.0 * VARLEN_H * int(n) * int(n) * VARLEN_D / 2 for n in lens))
+    tflops_var = flops_var / t_var / 1e12
+    log(f"varlen prefill ({VARLEN_B} sequences, {int(lens.sum())} tokens): {t_var * 1e6:.1f} us = "
+        f"{tflops_var:.1f} TFLOPS; padded to {Lmax}: {t_pad * 1e6:.1f} us")
+    del pads, po, pl, vq, vk, vv, vo, vl
+
     src_hash = kernel_source_hash()
     roof_pre = {
         "kernel": "fwd_kernel<128,64,causal>",
@@ -285,6 +326,11 @@ def main():
             "paged_decode_frac_of_peak": round(gbps_paged / PEAK_HBM_GBPS, 4),
             "paged_decode_us": round(t_paged * 1e6, 2),
             "paged_block_size": bs,
+            "varlen_prefill_tflops": round(tflops_var, 3),
+            "varlen_prefill_frac_of_peak": round(tflops_var / PEAK_FP16_TFLOPS, 4),
+            "varlen_prefill_us": round(t_var * 1e6, 2),
+            "varlen_tokens": int(lens.sum()),
+            "varlen_padded_us": round(t_pad * 1e6, 2),
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,
         },

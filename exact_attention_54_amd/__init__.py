@@ -8,6 +8,7 @@ library is missing or the tensors are not on a GPU, the call raises.
     o, lse = fa_fwd(q, k, v, causal=True)                  # q,k,v fp16 [B,H,S,D]
     o, lse = fa_decode_splitkv(q, k, v, num_splits=0)      # Sq == 1, 0 = auto
     o, lse = fa_decode_paged(q, k_cache, v_cache, block_tables, seq_lens)
+    o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)  # packed [total, H, D]
 """
 from __future__ import annotations
 
@@ -18,6 +19,7 @@ from ._capi import FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FA
 
 __all__ = [
     "fa_fwd",
+    "fa_fwd_varlen",
     "fa_decode_splitkv",
     "fa_decode_splitkv_ws",
     "fa_decode_paged",
@@ -90,6 +92,53 @@ def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None):
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream))
     _capi.check(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, o=None, lse=None,
+                  causal=False, scale=None, stream=None):
+    """Exact attention over a packed variable-length batch; returns (o, lse).
+
+    q fp16 [total_q, H, D]; k, v fp16 [total_k, H, D]; cu_seqlens_q / _k int32
+    [B + 1] on q's device; o fp16 like q; lse fp32 [H, total_q].  See
+    fa_fwd_varlen in include/fa.h.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float16 torch.Tensor on a GPU")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [total, H, D] tensor")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1:
+            raise TypeError(f"{name} must be a contiguous 1-d int32 torch.Tensor")
+    for t in (k, v, cu_seqlens_q, cu_seqlens_k):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on q's device")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 1 or cu_seqlens_k.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 entries")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if o.dtype != torch.float16 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous fp16 tensor shaped like q on its device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, total_q) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [H, total_q] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _capi.load()
+    st = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
+                           int(max_seqlen_q), int(max_seqlen_k), D, int(bool(causal)), float(scale),
+                           _stream(q, stream))
+    _capi.check(st, "fa_fwd_varlen")
     return o, lse
 
 

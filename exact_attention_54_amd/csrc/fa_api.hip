@@ -103,6 +103,36 @@ int launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* ls
   }
 }
 
+template <int D, int BN, int NW, bool CAUSAL>
+int launch_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, fa::VarlenArgs va, int B,
+                      float scale, hipStream_t stream) {
+  using Cfg = fa::FwdCfg<D, BN, NW>;
+  const int nqt = (va.max_q + Cfg::BM - 1) / Cfg::BM;
+  const int64_t BH = (int64_t)B * va.H;
+  const int64_t grid = (BH + 7) / 8 * 8 * nqt;  // slice count rounded up to a multiple of 8 (one per XCD)
+  if (grid > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  const float c2 = scale * fa::kLog2e;
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, 0, 0, (int)BH, nqt, c2, va);
+  return launched("fa_fwd_varlen kernel launch");
+}
+
+template <int D, bool CAUSAL>
+int launch_fwd_varlen_d(const void* q, const void* k, const void* v, void* o, float* lse, fa::VarlenArgs va, int B,
+                        float scale, hipStream_t stream) {
+  if constexpr (D == 256) {
+    return launch_fwd_varlen<256, 32, 4, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
+  } else {
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != FA_OK) return rc;
+    const int64_t wg8 = (int64_t)B * va.H * ((va.max_q + 255) / 256);
+    if (wg8 >= cus) return launch_fwd_varlen<D, 64, 8, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
+    return launch_fwd_varlen<D, 64, 4, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
+  }
+}
+
 template <int D>
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk,
                   float scale, hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
@@ -216,6 +246,30 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   }
 }
 
+int validate_varlen(const void* q, const void* k, const void* v, const void* o, const void* lse, const int* cu_q,
+                    const int* cu_k, int B, int H, int total_q, int total_k, int max_q, int max_k, int D,
+                    int causal, float scale) {
+  if (!q || !k || !v || !o || !lse || !cu_q || !cu_k) return fail(FA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || H < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d total_q=%d total_k=%d max_q=%d max_k=%d D=%d)",
+                B, H, total_q, total_k, max_q, max_k, D);
+  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
+    return fail(FA_ERR_INVALID_ARG, "lse and the cumulative lengths must be 4-byte aligned");
+  if (!product_le(total_q, H, D, 1, kMaxElems) || !product_le(total_k, H, D, 1, kMaxElems))
+    return fail(FA_ERR_INVALID_ARG, "tensor too large");
+  // one sequence of one head is addressed with 32-bit byte offsets, which
+  // also reach up to one query tile (256 rows) past its end
+  if ((int64_t)(max_q + 256) * H * D * 2 >= kMaxSliceBytes || (int64_t)(max_k + 256) * H * D * 2 >= kMaxSliceBytes)
+    return fail(FA_ERR_INVALID_ARG, "sequence too long: (max_seqlen + 256) * H * D * 2 must stay below 2 GiB");
+  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  return FA_OK;
+}
+
 int validate_paged(const void* q, const void* kc, const void* vc, const int* tables, const int* seq_lens,
                    const void* o, const void* lse, int B, int H, int D, int num_blocks, int block_size,
                    int max_blocks, float scale, int num_splits, int* lbs) {
@@ -279,6 +333,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     default:
       return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
                     : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+  }
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int B, int H, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int D, int causal, float scale, void* stream) {
+  int rc = validate_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q,
+                           max_seqlen_k, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  fa::VarlenArgs va = {cu_seqlens_q, cu_seqlens_k, H, total_q, total_k, max_seqlen_q, max_seqlen_k};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (D) {
+    case 64:
+      return causal ? launch_fwd_varlen_d<64, true>(q, k, v, o, lse, va, B, scale, s)
+                    : launch_fwd_varlen_d<64, false>(q, k, v, o, lse, va, B, scale, s);
+    case 128:
+      return causal ? launch_fwd_varlen_d<128, true>(q, k, v, o, lse, va, B, scale, s)
+                    : launch_fwd_varlen_d<128, false>(q, k, v, o, lse, va, B, scale, s);
+    default:
+      return causal ? launch_fwd_varlen_d<256, true>(q, k, v, o, lse, va, B, scale, s)
+                    : launch_fwd_varlen_d<256, false>(q, k, v, o, lse, va, B, scale, s);
   }
 }
 

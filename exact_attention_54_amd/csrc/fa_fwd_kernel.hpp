@@ -75,11 +75,23 @@ constexpr float kLazyRescale = 8.0f;
 template <int D, int NW>
 constexpr int fwd_wg_per_cu() { return (D <= 128 && NW == 4) ? 2 : 1; }
 
-template <int D, int BN, int NW, bool CAUSAL>
+// Packed variable-length batches ("Adaptive High-Performance Attention
+// Kernels in CUDA", Advanced Production Features, 3. Ragged / Variable-Length
+// Sequences): tokens of all sequences in one stream [total, H, D], sequence
+// b owning tokens cu[b] .. cu[b+1]-1.  Each workgroup reads its sequence's
+// bounds from the cumulative-length arrays and exits if its query tile lies
+// past the sequence's end.
+struct VarlenArgs {
+  const int* cu_q;  // [B + 1]
+  const int* cu_k;  // [B + 1]
+  int H, total_q, total_k, max_q, max_k;
+};
+
+template <int D, int BN, int NW, bool CAUSAL, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<D, NW>()))
 fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
            const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
-           int Sq, int Sk, int BH, int nqt, float c2) {
+           int Sq, int Sk, int BH, int nqt, float c2, VarlenArgs va = {}) {
   using C = FwdCfg<D, BN, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
@@ -94,24 +106,62 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // heaviest causal tiles first and, with B*H a multiple of 8, every tile
   // of a slice runs on the same XCD (workgroups are dealt to XCDs round
   // robin by id) and shares its L2.
-  const int rank = blockIdx.x / BH;
-  const int bh = blockIdx.x - rank * BH;
+  // Packed batches: workgroup id = (g * nqt + rank) * 8 + x for the slice
+  // bh = 8 g + x, so all query tiles of a slice run back to back on one XCD
+  // (ids are dealt to the 8 XCDs round robin) and share its L2 copy of the
+  // slice's K / V, whatever the number of slices.
+  const int rank = VARLEN ? (int)((blockIdx.x >> 3) % (unsigned)nqt) : (int)(blockIdx.x / BH);
+  const int bh = VARLEN ? (int)((blockIdx.x >> 3) / (unsigned)nqt) * 8 + (int)(blockIdx.x & 7)
+                        : (int)(blockIdx.x - rank * BH);
+  if (VARLEN && bh >= BH) return;  // the grid rounds the slice count up to a multiple of 8
+  // Slice of this work item: base pointers, lengths and the row stride (in
+  // elements) of q, k, v, o.  Dense [B, H, S, D]: rows D apart.  Packed
+  // [total, H, D]: rows H*D apart, lengths from the cumulative arrays
+  // (clamped into the tensors and to the maximum lengths the grid covers).
+  const _Float16 *qs, *ks_, *vs;
+  _Float16* os;
+  float* ls;
+  int RS;
+  if constexpr (VARLEN) {
+    const int b = bh / va.H;
+    const int h = bh - b * va.H;
+    const int sq0 = min(max(va.cu_q[b], 0), va.total_q);
+    const int sk0 = min(max(va.cu_k[b], 0), va.total_k);
+    Sq = min(min(max(va.cu_q[b + 1] - sq0, 0), va.total_q - sq0), va.max_q);
+    Sk = min(min(max(va.cu_k[b + 1] - sk0, 0), va.total_k - sk0), va.max_k);
+    nqt = (Sq + C::BM - 1) / C::BM;  // this sequence's tiles (the grid covers the longest)
+    if (rank >= nqt) return;  // the sequence has no query tile of this rank
+    RS = va.H * D;
+    qs = Q + ((size_t)sq0 * va.H + h) * D;
+    os = O + ((size_t)sq0 * va.H + h) * D;
+    ks_ = K + ((size_t)sk0 * va.H + h) * D;
+    vs = V + ((size_t)sk0 * va.H + h) * D;
+    ls = LSE + (size_t)h * va.total_q + sq0;
+  } else {
+    RS = D;
+    qs = Q + (size_t)bh * Sq * D;
+    os = O + (size_t)bh * Sq * D;
+    ks_ = K + (size_t)bh * Sk * D;
+    vs = V + (size_t)bh * Sk * D;
+    ls = LSE + (size_t)bh * Sq;
+  }
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
   const int q0 = qt * C::BM;
   const int qw = q0 + 32 * w;  // first query row of this wavefront
   const int qi = qw + r32;     // query row held by this lane
 
   // Per-slice buffer resources: rows past Sq / Sk read as zero and stores
-  // past Sq are dropped.
-  const auto rq = make_rsrc(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
-  const auto rk = make_rsrc(K + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
-  const auto rv = make_rsrc(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
-  const auto ro = make_rsrc(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  // past Sq are dropped (the extent ends with the last row's D elements).
+  auto extent = [&](int rows) { return rows > 0 ? (uint32_t)((rows - 1) * RS + D) * 2u : 0u; };
+  const auto rq = make_rsrc(qs, extent(Sq));
+  const auto rk = make_rsrc(ks_, extent(Sk));
+  const auto rv = make_rsrc(vs, extent(Sk));
+  const auto ro = make_rsrc(os, extent(Sq));
 
   // Q fragment: B operand of S^T = K Q^T, 8 consecutive d per lane and step.
   h8 qreg[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_h8(buf_load16(rq, ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u));
+  for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_h8(buf_load16(rq, ((uint32_t)qi * RS + 16 * ks + 8 * hh) * 2u));
 
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + C::BM, Sk) + BN - 1) / BN) : nkt_all;
@@ -128,18 +178,19 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const int p = (w * C::LPW + u) * 1024 + lane * 16;
     int r, c;
     swz_inv<C::KCH>(p >> 8, (p >> 4) & 15, r, c);
-    kgo[u] = (uint32_t)(r * D + c * 8) * 2;
+    kgo[u] = (uint32_t)(r * RS + c * 8) * 2;
     vswz_inv<C::KCH>(p >> 8, (p >> 4) & 15, r, c);
-    vgo[u] = (uint32_t)(r * D + c * 8) * 2;
+    vgo[u] = (uint32_t)(r * RS + c * 8) * 2;
   }
+  const uint32_t tile_stride = (uint32_t)BN * RS * 2;  // bytes between key tiles
   auto load_k = [&](int kt, int stage) {
-    const uint32_t tb = (uint32_t)kt * C::TILE_BYTES;
+    const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u)
       buf_load16_lds(rk, smem + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + kgo[u]);
   };
   auto load_v = [&](int kt, int stage) {
-    const uint32_t tb = (uint32_t)kt * C::TILE_BYTES;
+    const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u)
       buf_load16_lds(rv, smem + C::V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
@@ -352,7 +403,9 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  The O^T fragment is
   // transposed through LDS so each row leaves as coalesced 16-byte stores.
   const float l_tot = xhalf_sum(l_run);
-  const float inv = 1.f / l_tot;
+  // a row with no key at all (an empty key range of a packed sequence):
+  // O = 0, LSE = -inf
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   char* Os = smem + w * (32 * D * 2);
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
@@ -372,11 +425,11 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     for (int u = 0; u < (32 * D / 8) / 64; ++u) {
       const int ci = lane + 64 * u;
       const int row = ci / C::KCH, c = ci % C::KCH;
-      buf_store16(ro, ((uint32_t)(qw + row) * D + c * 8) * 2u,
+      buf_store16(ro, ((uint32_t)(qw + row) * RS + c * 8) * 2u,
                   *reinterpret_cast<const u32x4*>(Os + swz<C::KCH>(row, c)));
     }
   }
-  if (hh == 0 && qi < Sq) LSE[(size_t)bh * Sq + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+  if (hh == 0 && qi < Sq) ls[qi] = (l_tot > 0.f) ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 }  // namespace fa

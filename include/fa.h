@@ -84,6 +84,35 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_fwd_varlen -- fa_fwd over a packed batch of variable-length sequences
+ * ("Adaptive High-Performance Attention Kernels in CUDA", Advanced
+ * Production Features, 3. Ragged / Variable-Length Sequences: one token
+ * stream [total_tokens, H, d] indexed by cumulative sequence lengths, no
+ * padding).
+ *
+ *   q, o          fp16 [total_q, H, D], 16-byte aligned
+ *   k, v          fp16 [total_k, H, D], 16-byte aligned
+ *   lse           fp32 [H, total_q], 4-byte aligned
+ *   cu_seqlens_q  int32 [B + 1] device memory: sequence b owns query tokens
+ *   cu_seqlens_k  cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key tokens
+ *                 cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (4-byte aligned)
+ *   max_seqlen_q  upper bounds of the per-sequence lengths; the grid covers
+ *   max_seqlen_k  max_seqlen_q query rows per sequence and head
+ * Within each sequence the computation is fa_fwd's (causal = top-left
+ * aligned: query i of a sequence sees its keys 0..i).  Device-side values
+ * are not trusted: each start is clamped to [0, total] and each length to
+ * [0, min(total - start, max_seqlen)], so nothing outside the tensors is
+ * read or written.  Query rows that no sequence covers are left untouched;
+ * a query row whose sequence has no key gets o = 0 and lse = -inf.
+ * Limits: (max_seqlen + 256) * H * D * 2 < 2^31 bytes for q and for k.
+ * Errors as fa_fwd.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                  int causal, float scale, void* stream);
+
+/*
  * fa_decode_splitkv -- single-query decoding with the key range split into
  * num_splits contiguous partitions ("Adaptive High-Performance Attention
  * Kernels in CUDA", Advanced Production Features, 1. Split-K FlashDecoding).

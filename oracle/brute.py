@@ -99,3 +99,44 @@ def decode_paged_brute(q, k_cache, v_cache, block_tables, seq_lens, scale):
         O_all.append(O_b)
         L_all.append(L_b)
     return O_all, L_all
+
+
+def attention_varlen_brute(q, k, v, cu_q, cu_k, causal, scale):
+    """Packed variable-length attention with scalar loops over the flat
+    token stream: query token cu_q[b] + i of head h attends to key tokens
+    cu_k[b] + j (j <= i when causal) of the same head.  Inputs are nested
+    lists [total][H][D] and well-formed cumulative lengths.  Returns O as
+    nested lists [total_q][H][Dv] (None for rows no sequence covers) and LSE
+    [H][total_q]; a sequence without keys gives O = 0, LSE = -inf."""
+    total_q = len(q)
+    H = len(q[0])
+    Dv = len(v[0][0]) if len(v) else 0
+    O = [[None] * H for _ in range(total_q)]
+    L = [[None] * total_q for _ in range(H)]
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        for i in range(q1 - q0):
+            for h in range(H):
+                scores = []
+                for j in range(k1 - k0):
+                    if causal and j > i:
+                        continue
+                    dot = 0.0
+                    for d in range(len(q[q0 + i][h])):
+                        dot += float(q[q0 + i][h][d]) * float(k[k0 + j][h][d])
+                    scores.append((j, scale * dot))
+                if not scores:
+                    O[q0 + i][h] = [0.0] * Dv
+                    L[h][q0 + i] = -math.inf
+                    continue
+                mx = max(s for _, s in scores)
+                den = 0.0
+                row = [0.0] * Dv
+                for j, s in scores:
+                    e = math.exp(s - mx)
+                    den += e
+                    for d in range(Dv):
+                        row[d] += e * float(v[k0 + j][h][d])
+                O[q0 + i][h] = [x / den for x in row]
+                L[h][q0 + i] = mx + math.log(den)
+    return O, L

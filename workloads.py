@@ -21,6 +21,11 @@ are scattered through the cache as they would be after many allocations and
 frees.  Pages that no table entry names are filled with NaN, so a read of one
 would show up in the result.
 
+Packed variable-length batches (``make_varlen``) use the same recipe over the
+packed [total_tokens, H, D] shape (Q, then K, then V), with sequence lengths
+drawn uniformly from a range by a seeded generator of their own; the
+cumulative lengths start at 0 and cover every token.
+
 The shapes follow the pages' workloads: the LLaMA-7B prefill shape
 (1, 32, 4096, 4096, 128) and the 8K-context single-query decode shape of the
 "FlashAttention-2 MMA" benchmark tables, the B8/H16/S256/D64 shape of
@@ -111,6 +116,33 @@ def to_pages(x: np.ndarray, tables: np.ndarray, num_blocks: int, block_size: int
             lo, hi = j * block_size, min(S, (j + 1) * block_size)
             pages[tables[b, j], :, : hi - lo, :] = x[b, :, lo:hi, :]
     return pages
+
+
+# Packed variable-length prefill: 16 sequences of 256..4096 tokens (LLaMA-7B
+# heads), the ragged counterpart of the 4096-token prefill.
+VARLEN_B, VARLEN_H, VARLEN_D = 16, 32, 128
+VARLEN_MIN, VARLEN_MAX = 256, 4096
+VARLEN_LEN_SEED, VARLEN_SEED = 8, 7
+
+
+def varlen_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """B sequence lengths drawn uniformly from [lo, hi]."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    return gen.integers(lo, hi + 1, size=B).astype(np.int64)
+
+
+def make_varlen(lengths, H: int, D: int, seed: int, lengths_k=None):
+    """Packed q [total_q, H, D] and k, v [total_k, H, D] fp16 (N(0,1) draws,
+    Q then K then V) with their cumulative lengths [B + 1] int32."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    lengths_k = lengths if lengths_k is None else np.asarray(lengths_k, dtype=np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lengths_k)]).astype(np.int32)
+    gen = np.random.Generator(np.random.PCG64(seed))
+    q = _draw_fp16(gen, (int(cu_q[-1]), H, D)) if cu_q[-1] > 0 else np.zeros((0, H, D), np.float16)
+    k = _draw_fp16(gen, (int(cu_k[-1]), H, D)) if cu_k[-1] > 0 else np.zeros((0, H, D), np.float16)
+    v = _draw_fp16(gen, (int(cu_k[-1]), H, D)) if cu_k[-1] > 0 else np.zeros((0, H, D), np.float16)
+    return q, k, v, cu_q, cu_k
 
 
 def sample_rows(w: Workload, count: int, seed: int = 12345):
