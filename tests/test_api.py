@@ -160,3 +160,83 @@ def test_python_binding_refuses_cpu_tensors():
         fa.fa_fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.fa_fwd(q.float(), q, q)
+
+
+# ------------------------------------------------ packed (ragged) prefill
+
+VGOOD = dict(B=2, H=3, total_q=9, total_k=11, max_q=5, max_k=6, D=64, causal=1, scale=0.125)
+CU = [A + 0x5000, A + 0x6000]  # fake cumulative-length arrays
+
+
+def varlen(lib, p=P, cu=CU, **kw):
+    a = dict(VGOOD, **kw)
+    return lib.fa_fwd_varlen(p[0], p[1], p[2], p[3], p[4], cu[0], cu[1], a["B"], a["H"], a["total_q"],
+                             a["total_k"], a["max_q"], a["max_k"], a["D"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(H=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(total_q=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(total_k=-3), _capi.FA_ERR_INVALID_ARG),
+    (dict(max_q=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(max_k=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(D=96), _capi.FA_ERR_UNSUPPORTED),
+    (dict(causal=3), _capi.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _capi.FA_ERR_INVALID_ARG),
+    (dict(max_q=1 << 24, H=64, D=128), _capi.FA_ERR_INVALID_ARG),   # one sequence past 2 GiB
+    (dict(max_k=(1 << 24) - 200, H=32, D=128), _capi.FA_ERR_INVALID_ARG),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert varlen(lib, **kw) == code
+    assert _capi.last_error() != ""
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_varlen_rejects_null_and_misaligned(lib, idx):
+    ptrs = list(P) + list(CU)
+    ptrs[idx] = 0
+    assert varlen(lib, p=ptrs[:5], cu=ptrs[5:]) == _capi.FA_ERR_INVALID_ARG
+    ptrs = list(P) + list(CU)
+    ptrs[idx] += 2  # below every alignment the entry point asks for
+    assert varlen(lib, p=ptrs[:5], cu=ptrs[5:]) == _capi.FA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------ paged decoding
+
+PGOOD = dict(B=2, H=3, D=64, num_blocks=10, block_size=16, max_blocks=4, scale=0.125, ns=2)
+TBL = [A + 0x5000, A + 0x6000]  # fake block table and context lengths
+
+
+def paged(lib, p=P, t=TBL, **kw):
+    a = dict(PGOOD, **kw)
+    return lib.fa_decode_paged(p[0], p[1], p[2], t[0], t[1], p[3], p[4], a["B"], a["H"], a["D"],
+                               a["num_blocks"], a["block_size"], a["max_blocks"], a["scale"], None, a["ns"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(H=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(max_blocks=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(block_size=0), _capi.FA_ERR_INVALID_ARG),
+    (dict(block_size=12), _capi.FA_ERR_INVALID_ARG),     # not a power of two
+    (dict(block_size=2048), _capi.FA_ERR_INVALID_ARG),   # above 1024
+    (dict(D=32), _capi.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), _capi.FA_ERR_INVALID_ARG),
+    (dict(ns=65), _capi.FA_ERR_INVALID_ARG),             # more splits than the table reaches (4 * 16)
+    (dict(max_blocks=1 << 21, block_size=1024), _capi.FA_ERR_INVALID_ARG),
+])
+def test_paged_rejects(lib, kw, code):
+    assert paged(lib, **kw) == code
+    assert _capi.last_error() != ""
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_paged_rejects_null_and_misaligned(lib, idx):
+    ptrs = list(P[:3]) + list(TBL) + list(P[3:])
+    ptrs[idx] = 0
+    assert paged(lib, p=ptrs[:3] + ptrs[5:], t=ptrs[3:5]) == _capi.FA_ERR_INVALID_ARG
+    ptrs = list(P[:3]) + list(TBL) + list(P[3:])
+    ptrs[idx] += 2
+    assert paged(lib, p=ptrs[:3] + ptrs[5:], t=ptrs[3:5]) == _capi.FA_ERR_INVALID_ARG
