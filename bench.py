@@ -8,8 +8,8 @@ One step = the whole path once over one batch of synthetic fp16 N(0,1) input:
 After the timed steps, paged decoding (fa_decode_paged) of the same K / V in
 16-token pages, and packed variable-length causal prefill (fa_fwd_varlen) of
 16 sequences of 256..4096 tokens (with the same batch zero-padded through
-fa_fwd for comparison), are timed on their own and reported beside the step
-figures.
+fa_fwd for comparison), and the backward pass (fa_bwd) of the causal
+prefill, are timed on their own and reported beside the step figures.
 Inputs are resident in HBM before the timed region.  Prefill throughput
 counts 4*B*H*Sq*Sk*D FLOPs halved for the causal mask; decode throughput
 counts the bytes of K and V read.  rank 0 prints one JSON line on stdout;
@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd TFLOPS (causal prefill D=128) + decode K/V GB/s, % of roofline"
-KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_kernel.hpp", "fa_decode_kernel.hpp", "fa_api.hip"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_kernel.hpp", "fa_decode_kernel.hpp", "fa_bwd_kernel.hpp", "fa_api.hip"]
 
 
 def log(msg):
@@ -152,7 +152,7 @@ def main():
     import torch
 
     import exact_attention_54_amd as fa
-    from workloads import (PAGED_BLOCK_SIZE, PAGED_PERM_SEED, VARLEN_B, VARLEN_D, VARLEN_H, VARLEN_LEN_SEED,
+    from workloads import (make_qkv, PAGED_BLOCK_SIZE, PAGED_PERM_SEED, VARLEN_B, VARLEN_D, VARLEN_H, VARLEN_LEN_SEED,
                            VARLEN_MAX, VARLEN_MIN, VARLEN_SEED, WORKLOADS, make_varlen, paged_layout,
                            varlen_lengths, workload_inputs)
 
@@ -278,6 +278,22 @@ def main():
         f"{tflops_var:.1f} TFLOPS; padded to {Lmax}: {t_pad * 1e6:.1f} us")
     del pads, po, pl, vq, vk, vv, vo, vl
 
+    # Backward of the causal prefill (fa_bwd: D, dK/dV, dQ kernels) from the
+    # forward's o and lse with a seeded fp16 dO, timed back to back.
+    do3 = torch.from_numpy(make_qkv(w3.B, w3.H, w3.Sq, 1, w3.D, 13)[0]).to(dev)
+    prefill()
+    dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+
+    def backward():
+        fa.fa_bwd(q3, k3, v3, o3, l3, do3, dq3, dk3, dv3, causal=True, scale=w3.scale)
+
+    for _ in range(args.warmup):
+        backward()
+    t_bwd = time_launches(torch, backward, args.steps)
+    tflops_bwd = 2.5 * flops / t_bwd / 1e12
+    log(f"backward (causal prefill shape): {t_bwd * 1e6:.1f} us = {tflops_bwd:.1f} TFLOPS (2.5 x forward FLOPs)")
+    del dq3, dk3, dv3, do3
+
     src_hash = kernel_source_hash()
     roof_pre = {
         "kernel": "fwd_kernel<128,64,causal>",
@@ -331,6 +347,9 @@ def main():
             "varlen_prefill_us": round(t_var * 1e6, 2),
             "varlen_tokens": int(lens.sum()),
             "varlen_padded_us": round(t_pad * 1e6, 2),
+            "backward_tflops": round(tflops_bwd, 3),
+            "backward_frac_of_peak": round(tflops_bwd / PEAK_FP16_TFLOPS, 4),
+            "backward_us": round(t_bwd * 1e6, 2),
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,
         },

@@ -9,6 +9,7 @@ library is missing or the tensors are not on a GPU, the call raises.
     o, lse = fa_decode_splitkv(q, k, v, num_splits=0)      # Sq == 1, 0 = auto
     o, lse = fa_decode_paged(q, k_cache, v_cache, block_tables, seq_lens)
     o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)  # packed [total, H, D]
+    dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal=True)
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ from ._capi import FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FA
 __all__ = [
     "fa_fwd",
     "fa_fwd_varlen",
+    "fa_bwd",
     "fa_decode_splitkv",
     "fa_decode_splitkv_ws",
     "fa_decode_paged",
@@ -93,6 +95,32 @@ def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None):
                     B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream))
     _capi.check(st, "fa_fwd")
     return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, causal=False, scale=None, stream=None):
+    """Gradients (dq, dk, dv) of exact attention from fa_fwd's o and lse.  See fa_bwd in include/fa.h."""
+    torch = _torch()
+    B, H, Sq, Sk, D = _check_qkv(q, k, v)
+    for name, t, shape in (("o", o, q.shape), ("do", do, q.shape)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or tuple(t.shape) != tuple(shape) \
+                or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous fp16 tensor shaped like q on its device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [B, H, Sq] tensor on q's device")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.float16 or t.shape != ref.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous fp16 tensor shaped like its input")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _capi.load()
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
+                    _stream(q, stream))
+    _capi.check(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, o=None, lse=None,

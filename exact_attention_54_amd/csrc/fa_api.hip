@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "fa_bwd_kernel.hpp"
 #include "fa_decode_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
 
@@ -163,6 +164,36 @@ int launch_decode_paged(const void* q, const void* kc, const void* vc, const int
   hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
                      static_cast<_Float16*>(o), lse, ns);
   return launched("paged decode merge launch");
+}
+
+template <int D, bool CAUSAL>
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int BH, int Sq, int Sk, float scale, hipStream_t stream, float* dvec) {
+  constexpr int NW = 4;
+  constexpr int LPR = (D / 8 < 16) ? D / 8 : 16;
+  const int64_t rows = (int64_t)BH * Sq;
+  const int64_t dot_grid = (rows * LPR + 255) / 256;
+  const int64_t kv_grid = (int64_t)((Sk + 32 * NW - 1) / (32 * NW)) * BH;
+  const int nqt = (Sq + 32 * NW - 1) / (32 * NW);
+  const int64_t q_grid = (int64_t)nqt * BH;
+  if (dot_grid > kMaxGrid || kv_grid > kMaxGrid || q_grid > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  const auto* Q = static_cast<const _Float16*>(q);
+  const auto* K = static_cast<const _Float16*>(k);
+  const auto* V = static_cast<const _Float16*>(v);
+  const auto* dO = static_cast<const _Float16*>(dout);
+  float* l2 = dvec + rows;  // LSE in log2 units
+  hipLaunchKernelGGL((fa::bwd_dot_kernel<D>), dim3((unsigned)dot_grid), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(o), dO, lse, dvec, l2, rows);
+  int rc = launched("fa_bwd preprocess launch");
+  if (rc != FA_OK) return rc;
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, NW, CAUSAL>), dim3((unsigned)kv_grid), dim3(64 * NW), 0, stream, Q, K, V,
+                     dO, l2, dvec, static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), Sq, Sk, BH,
+                     (int)(kv_grid / BH), scale);
+  rc = launched("fa_bwd dK/dV launch");
+  if (rc != FA_OK) return rc;
+  hipLaunchKernelGGL((fa::bwd_dq_kernel<D, NW, CAUSAL>), dim3((unsigned)q_grid), dim3(64 * NW), 0, stream, Q, K, V, dO,
+                     l2, dvec, static_cast<_Float16*>(dq), Sq, Sk, BH, nqt, scale);
+  return launched("fa_bwd dQ launch");
 }
 
 std::atomic<int> g_cu_count[64];
@@ -355,6 +386,36 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
       return causal ? launch_fwd_varlen_d<256, true>(q, k, v, o, lse, va, B, scale, s)
                     : launch_fwd_varlen_d<256, false>(q, k, v, o, lse, va, B, scale, s);
   }
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D, int causal, float scale,
+           void* stream) {
+  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
+  if (D == 256) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
+  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipMemPool_t pool = nullptr;
+  rc = workspace_pool(&pool);
+  if (rc != FA_OK) return rc;
+  void* ws = nullptr;
+  const size_t bytes = ((size_t)B * H * Sq * 8 + 255) / 256 * 256;  // D and LSE in log2 units
+  rc = hip_check(hipMallocFromPoolAsync(&ws, bytes, pool, s), "workspace allocation");
+  if (rc != FA_OK) return rc;
+  float* dvec = static_cast<float*>(ws);
+  const int BH = B * H;
+  if (D == 64)
+    rc = causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+  else
+    rc = causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
+  return rc != FA_OK ? rc : frc;
 }
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {

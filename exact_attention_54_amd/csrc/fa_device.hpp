@@ -111,6 +111,32 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
 }
 
+// The same copy issued from inline asm, for loops that order the copies
+// themselves: the compiler then does not count them as pending LDS writes
+// (it would wait for all of them before every LDS read it cannot tell
+// apart), so the caller waits with s_waitcnt vmcnt before the barrier that
+// publishes the data.  rs: the four descriptor dwords; lds_addr: the
+// wave-uniform LDS byte address (M0) that lane l's 16 (dma16) or 4 (dma4)
+// bytes land at plus 16 l (4 l).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xffffu;
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr));
+}
+__device__ __forceinline__ void dma4(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr));
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 // Maximum / sum of x over the two 32-lane halves of a wavefront, on the
 // VALU: v_permlane32_swap(x, x) returns the low half of x in both halves
 // and the high half in both halves (pinned by a GPU probe test).

@@ -84,6 +84,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_bwd -- gradients of exact attention from the forward's outputs
+ * ("Adaptive High-Performance Attention Kernels in CUDA", Advanced
+ * Production Features, 2. Custom CUDA Backward Pass: S and P recomputed
+ * from the forward statistics, D_i = sum_d dO_id O_id, dS = P o (dP - D)).
+ *
+ *   q, k, v, o, lse  as passed to / returned by fa_fwd with the same B, H,
+ *                    Sq, Sk, D, causal and scale (lse: natural log)
+ *   dout             fp16 [B, H, Sq, D], the gradient of the loss w.r.t. o
+ *   dq               fp16 [B, H, Sq, D]  = scale * dS K
+ *   dk, dv           fp16 [B, H, Sk, D]  dk = scale * dS^T Q, dv = P^T dO
+ * with P = exp(scale * Q K^T + mask - lse), dP = dout V^T.  All tensors are
+ * caller-owned device memory, 16-byte aligned (lse 4-byte); outputs must not
+ * overlap inputs.  A per-row workspace (D and the LSE in log2 units,
+ * 2*B*H*Sq fp32) comes from the same
+ * per-device pool as fa_decode_splitkv.  Four kernels run on `stream`.
+ * Supports D in {64, 128} (D = 256: FA_ERR_UNSUPPORTED); other errors as
+ * fa_fwd.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+           int causal, float scale, void* stream);
+
+/*
  * fa_fwd_varlen -- fa_fwd over a packed batch of variable-length sequences
  * ("Adaptive High-Performance Attention Kernels in CUDA", Advanced
  * Production Features, 3. Ragged / Variable-Length Sequences: one token

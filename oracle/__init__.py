@@ -15,12 +15,14 @@ Contents
   paged.decode_paged      single-query decoding over a paged KV cache (block tables)
   paged.gather_context    the present context rows of one sequence, in token order
   varlen.attention_varlen attention over a packed batch of variable-length sequences
+  backward.attention_backward  dQ, dK, dV of the definition (fp64)
   brute.attention_brute   pure-Python scalar loops, for tiny inputs only
   brute.decode_paged_brute  paged decoding with scalar loops and explicit table lookups
   brute.attention_varlen_brute  packed variable-length attention with scalar loops
 
 Every function is pinned by tests in ``tests/test_oracle.py`` and
-``tests/test_oracle_paged.py`` and ``tests/test_oracle_varlen.py`` against
+``tests/test_oracle_paged.py``, ``tests/test_oracle_varlen.py`` and
+``tests/test_oracle_backward.py`` against
 closed forms, hand-derived worked examples (``tests/golden/``), invariants of
 the definition, brute force and ``torch.nn.functional.scaled_dot_product_attention``
 in fp64 on the CPU.  No function here is "parity unpinned".
@@ -37,6 +39,7 @@ from .dense import (
 from .brute import attention_brute, attention_varlen_brute, decode_paged_brute
 from .paged import decode_paged, gather_context
 from .varlen import attention_varlen, sequence_bounds
+from .backward import attention_backward
 
 __all__ = [
     "attention",
@@ -53,4 +56,5 @@ __all__ = [
     "attention_varlen",
     "sequence_bounds",
     "attention_varlen_brute",
+    "attention_backward",
 ]
