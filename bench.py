@@ -33,7 +33,8 @@ if ROOT not in sys.path:
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd TFLOPS (causal prefill D=128) + decode K/V GB/s, % of roofline"
-KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_kernel.hpp", "fa_decode_kernel.hpp", "fa_bwd_kernel.hpp", "fa_api.hip"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_kernel.hpp", "fa_splitd_kernel.hpp", "fa_decode_kernel.hpp", "fa_bwd_kernel.hpp",
+                  "fa_api.hip"]
 
 
 def log(msg):
@@ -294,6 +295,28 @@ def main():
     log(f"backward (causal prefill shape): {t_bwd * 1e6:.1f} us = {tflops_bwd:.1f} TFLOPS (2.5 x forward FLOPs)")
     del dq3, dk3, dv3, do3
 
+    # Split-D forward on the large-head shapes (D = 512 and 1024), both masks,
+    # timed back to back; FLOPs counted as for the prefill above.
+    splitd = {}
+    for name in ("d512_prefill", "d1024_prefill"):
+        w = WORKLOADS[name]
+        qx, kx, vx = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
+        ox = torch.empty_like(qx)
+        lx = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+        for causal in (False, True):
+            def large_head():
+                fa.fa_fwd(qx, kx, vx, ox, lx, causal=causal, scale=w.scale)
+
+            for _ in range(args.warmup):
+                large_head()
+            t = time_launches(torch, large_head, args.steps)
+            tf = prefill_flops(w.B, w.H, w.Sq, w.Sk, w.D, causal) / t / 1e12
+            tag = f"{name}_{'causal' if causal else 'full'}"
+            splitd[tag + "_us"] = round(t * 1e6, 2)
+            splitd[tag + "_tflops"] = round(tf, 3)
+            log(f"split-D {name} causal={causal}: {t * 1e6:.1f} us = {tf:.1f} TFLOPS")
+        del qx, kx, vx, ox, lx
+
     src_hash = kernel_source_hash()
     roof_pre = {
         "kernel": "fwd_kernel<128,64,causal>",
@@ -350,6 +373,7 @@ def main():
             "backward_tflops": round(tflops_bwd, 3),
             "backward_frac_of_peak": round(tflops_bwd / PEAK_FP16_TFLOPS, 4),
             "backward_us": round(t_bwd * 1e6, 2),
+            **{"splitd_" + k: x for k, x in splitd.items()},
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,
         },

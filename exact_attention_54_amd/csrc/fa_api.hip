@@ -15,6 +15,7 @@
 #include "fa_bwd_kernel.hpp"
 #include "fa_decode_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
+#include "fa_splitd_kernel.hpp"
 
 namespace {
 
@@ -50,7 +51,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d Sq=%d Sk=%d D=%d)", B, H, Sq, Sk, D);
-  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024)
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256, 512, 1024}", D);
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
@@ -132,6 +134,20 @@ int launch_fwd_varlen_d(const void* q, const void* k, const void* v, void* o, fl
     if (wg8 >= cus) return launch_fwd_varlen<D, 64, 8, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
     return launch_fwd_varlen<D, 64, 4, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
   }
+}
+
+// Head dims above 256: Split-D, one workgroup of D/128 wavefronts per 32
+// query rows.
+template <int D, bool CAUSAL>
+int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+                      float scale, hipStream_t stream) {
+  const int nqt = (Sq + 31) / 32;
+  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  hipLaunchKernelGGL((fa::fwd_splitd_kernel<D, CAUSAL>), dim3(nqt * BH), dim3(fa::SplitDCfg<D>::THREADS), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt,
+                     scale * fa::kLog2e);
+  return launched("fa_fwd Split-D kernel launch");
 }
 
 template <int D>
@@ -259,6 +275,7 @@ int validate_decode(const void* q, const void* k, const void* v, const void* o, 
                     int Sq, int Sk, int D, int causal, float scale, int num_splits) {
   int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
   if (rc != FA_OK) return rc;
+  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "split-KV decoding supports head dims 64, 128, 256");
   if (Sq != 1) return fail(FA_ERR_INVALID_ARG, "split-KV decoding needs Sq == 1 (got %d)", Sq);
   if (causal != 0) return fail(FA_ERR_INVALID_ARG, "split-KV decoding is non-causal");
   if (num_splits > Sk) return fail(FA_ERR_INVALID_ARG, "num_splits %d exceeds Sk %d", num_splits, Sk);
@@ -361,9 +378,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     case 128:
       return causal ? launch_fwd_d<128, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
                     : launch_fwd_d<128, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
-    default:
+    case 256:
       return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
                     : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+    case 512:
+      return causal ? launch_fwd_splitd<512, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_splitd<512, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+    default:
+      return causal ? launch_fwd_splitd<1024, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_splitd<1024, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
   }
 }
 
@@ -396,7 +419,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
-  if (D == 256) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
+  if (D > 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
   if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;

@@ -10,6 +10,7 @@ namespace fa {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -36,7 +37,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // line of gfx950.
 template <int C>
 __device__ __forceinline__ uint32_t swz(int r, int c) {
-  static_assert(C == 4 || C == 8 || C == 16 || C == 32, "chunks per row");
+  static_assert(C == 4 || C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
   if constexpr (C >= 16) {
     const int line = r * (C / 16) + (c >> 4);
     const int slot = (c & 15) ^ (r & 15);
@@ -69,7 +70,7 @@ __device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
 // of a 256-byte line.
 template <int C>
 __device__ __forceinline__ uint32_t vswz(int r, int c) {
-  static_assert(C == 8 || C == 16 || C == 32, "chunks per row");
+  static_assert(C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
   if constexpr (C >= 16) {
     const int line = r * (C / 16) + (c >> 4);
     const int slot = (c & 15) ^ (4 * (r & 3));

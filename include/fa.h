@@ -61,7 +61,7 @@ extern "C" {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size out of range, bad scale, ... */
-  FA_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128, 256} */
+  FA_ERR_UNSUPPORTED = 2, /* head dim not supported by the entry point */
   FA_ERR_HIP = 3          /* a HIP call or kernel launch failed */
 };
 
@@ -70,14 +70,18 @@ enum fa_status {
  *
  *   q      [B, H, Sq, D] fp16        k, v  [B, H, Sk, D] fp16
  *   o      [B, H, Sq, D] fp16 out    lse   [B, H, Sq]    fp32 out
- *   B, H, Sq, Sk >= 1;  D in {64, 128, 256};  causal 0 or 1;  scale > 0.
+ *   B, H, Sq, Sk >= 1;  D in {64, 128, 256, 512, 1024};  causal 0 or 1;
+ *   scale > 0.
  *
  * Queries are split into tiles, one workgroup each ("Split-Q" in
  * "FlashAttention-2 MMA", Supported Dispatch Strategies; loop order of
  * "Adaptive High-Performance Attention Kernels in CUDA", Architectural
  * Progression, Stage 3).  With causal = 1 the key tiles that lie wholly
- * above the diagonal are never loaded (same page, Lever A).  Any Sq works,
- * including Sq = 1.  o and lse must not overlap the inputs.
+ * above the diagonal are never loaded (same page, Lever A).  Head dims 512
+ * and 1024 take the Split-D kernel (same strategy list, 3. Split-D): the
+ * D/128 wavefronts of a workgroup share 32 query rows, each owns a 128-wide
+ * slice of D, and their partial scores are summed through LDS.  Any Sq
+ * works, including Sq = 1.  o and lse must not overlap the inputs.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Sq, int Sk, int D, int causal, float scale,
@@ -141,7 +145,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * Kernels in CUDA", Advanced Production Features, 1. Split-K FlashDecoding).
  *
  * Same arguments as fa_fwd plus num_splits; requires Sq == 1 and causal == 0
- * (FA_ERR_INVALID_ARG otherwise).  Partition s covers keys
+ * (FA_ERR_INVALID_ARG otherwise) and D in {64, 128, 256}
+ * (FA_ERR_UNSUPPORTED otherwise).  Partition s covers keys
  * [s*c, min((s+1)*c, Sk)) with c = ceil(Sk / num_splits); trailing
  * partitions may be empty.  num_splits <= 0 picks fa_decode_auto_splits()
  * for the current device; otherwise 1 <= num_splits <= Sk.

@@ -62,7 +62,8 @@ def dec_ws(lib, ws=A + 0x8000, nbytes=1 << 20, p=P, ns=2, **kw):
     (dict(D=0), _capi.FA_ERR_INVALID_ARG),
     (dict(D=96), _capi.FA_ERR_UNSUPPORTED),
     (dict(D=32), _capi.FA_ERR_UNSUPPORTED),
-    (dict(D=512), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=2048), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=384), _capi.FA_ERR_UNSUPPORTED),
     (dict(causal=2), _capi.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), _capi.FA_ERR_INVALID_ARG),
     (dict(scale=-0.5), _capi.FA_ERR_INVALID_ARG),
@@ -240,3 +241,15 @@ def test_paged_rejects_null_and_misaligned(lib, idx):
     ptrs = list(P[:3]) + list(TBL) + list(P[3:])
     ptrs[idx] += 2
     assert paged(lib, p=ptrs[:3] + ptrs[5:], t=ptrs[3:5]) == _capi.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("D", [512, 1024])
+def test_large_heads_only_through_fa_fwd(lib, D):
+    # Split-D serves fa_fwd; decoding, paged decoding, packed prefill and the
+    # backward refuse head dims above 256 before any HIP call
+    assert dec(lib, D=D) == _capi.FA_ERR_UNSUPPORTED
+    assert paged(lib, D=D) == _capi.FA_ERR_UNSUPPORTED
+    assert varlen(lib, D=D) == _capi.FA_ERR_UNSUPPORTED
+    a = dict(GOOD, D=D)
+    assert lib.fa_bwd(P[0], P[1], P[2], P[3], P[4], A + 0x5000, A + 0x6000, A + 0x7000, A + 0x8000, a["B"], a["H"],
+                      a["Sq"], a["Sk"], D, a["causal"], a["scale"], None) == _capi.FA_ERR_UNSUPPORTED

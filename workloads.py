@@ -29,7 +29,9 @@ cumulative lengths start at 0 and cover every token.
 The shapes follow the pages' workloads: the LLaMA-7B prefill shape
 (1, 32, 4096, 4096, 128) and the 8K-context single-query decode shape of the
 "FlashAttention-2 MMA" benchmark tables, the B8/H16/S256/D64 shape of
-"Flash Attention 101"'s A100 benchmark, and a D=256 large-head prefill.
+"Flash Attention 101"'s A100 benchmark, a D=256 large-head prefill, and the
+"Large Head" (D = 512) and "Massive Head" (D = 1024) shapes of the
+"FlashAttention-2 MMA" benchmark matrix.
 """
 from __future__ import annotations
 
@@ -68,6 +70,9 @@ WORKLOADS = {
     "llama7b_prefill": Workload("llama7b_prefill", 1, 32, 4096, 4096, 128, (True,), 3, "prefill"),
     "decode_8k": Workload("decode_8k", 16, 32, 1, 8192, 128, (False,), 4, "decode"),
     "d256_prefill": Workload("d256_prefill", 1, 16, 2048, 2048, 256, (True,), 5, "prefill"),
+    # large heads (Split-D)
+    "d512_prefill": Workload("d512_prefill", 1, 8, 1024, 1024, 512, (False, True), 9, "prefill"),
+    "d1024_prefill": Workload("d1024_prefill", 1, 4, 512, 512, 1024, (False, True), 10, "prefill"),
 }
 
 
