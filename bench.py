@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="before the warmup steps, run untimed steps for this long so the GPU clocks have "
+                         "left their idle state (they take ~10 ms of load to ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library's automatic choice")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -185,6 +188,16 @@ def main():
         prefill()
         decode()
 
+    # clock spin-up: from idle the GPU needs ~10 ms of load before its clocks
+    # settle, so a short warmup alone would leave the first timed steps slow
+    t0, n_spin = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < args.spinup_ms:
+        step()
+        n_spin += 1
+        if n_spin % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"spin-up: {n_spin} untimed steps in {(time.perf_counter() - t0) * 1e3:.0f} ms")
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <mutex>
@@ -140,14 +141,18 @@ int launch_fwd_varlen_d(const void* q, const void* k, const void* v, void* o, fl
 // query rows.
 template <int D, bool CAUSAL>
 int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-                      float scale, hipStream_t stream) {
+                      float scale, hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
   const int nqt = (Sq + 31) / 32;
-  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  hipLaunchKernelGGL((fa::fwd_splitd_kernel<D, CAUSAL>), dim3(nqt * BH), dim3(fa::SplitDCfg<D>::THREADS), 0, stream,
-                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt,
-                     scale * fa::kLog2e);
-  return launched("fa_fwd Split-D kernel launch");
+  hipLaunchKernelGGL((fa::fwd_splitd_kernel<D, CAUSAL>), dim3(nqt * BH * ns), dim3(fa::SplitDCfg<D>::THREADS), 0,
+                     stream, static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt, ns,
+                     scale * fa::kLog2e, ws_o, ws_lse);
+  int rc = launched("fa_fwd Split-D kernel launch");
+  if (rc != FA_OK || ns == 1) return rc;
+  // combine the key parts of every query row: rows of [BH * Sq, ns, D]
+  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH * Sq), dim3(256), 0, stream, ws_o, ws_lse,
+                     static_cast<_Float16*>(o), lse, ns);
+  return launched("fa_fwd Split-D merge launch");
 }
 
 template <int D>
@@ -271,6 +276,47 @@ size_t ws_bytes(int64_t BH, int D, int ns) {
   return (floats * 4 + 255) / 256 * 256;
 }
 
+// Key parts for the Split-D forward: 1 when the (query tile, slice) work
+// items give every CU one, else enough parts to do so, each of at least two
+// key tiles, at most 16.  (A second co-resident workgroup per CU, which the
+// D = 512 kernel's LDS would allow, measured slower once the merge is paid:
+// the CU's LDS and copy bandwidth is already the limit.)
+int splitd_parts(int64_t work_items, int nkt_all, int cus) {
+  if (work_items >= cus) return 1;
+  int64_t ns = (cus + work_items - 1) / work_items;
+  ns = std::min<int64_t>(ns, std::max(1, nkt_all / 2));
+  ns = std::min<int64_t>(ns, 16);
+  return (int)std::max<int64_t>(ns, 1);
+}
+
+template <int D>
+int run_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+                   int causal, float scale, hipStream_t s) {
+  const int nqt = (Sq + 31) / 32;
+  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  int cus = 0;
+  int rc = device_cu_count(&cus);
+  if (rc != FA_OK) return rc;
+  const int ns = splitd_parts((int64_t)nqt * BH, (Sk + 31) / 32, cus);
+  void* ws = nullptr;
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  if (ns > 1) {
+    hipMemPool_t pool = nullptr;
+    rc = workspace_pool(&pool);
+    if (rc != FA_OK) return rc;
+    rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)BH * Sq, D, ns), pool, s), "workspace allocation");
+    if (rc != FA_OK) return rc;
+    ws_o = static_cast<float*>(ws);
+    ws_lse = ws_o + (size_t)BH * Sq * ns * D;
+  }
+  rc = causal ? launch_fwd_splitd<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse)
+              : launch_fwd_splitd<D, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse);
+  if (!ws) return rc;
+  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
+  return rc != FA_OK ? rc : frc;
+}
+
 int validate_decode(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
                     int Sq, int Sk, int D, int causal, float scale, int num_splits) {
   int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
@@ -382,11 +428,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
       return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
                     : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
     case 512:
-      return causal ? launch_fwd_splitd<512, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_splitd<512, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+      return run_fwd_splitd<512>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s);
     default:
-      return causal ? launch_fwd_splitd<1024, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_splitd<1024, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
+      return run_fwd_splitd<1024>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s);
   }
 }
 

@@ -11,12 +11,16 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Online softmax: row-max growth (log2 units) tolerated before the reference
+// max moves (then O and l are rescaled); in between p <= 2^8.
+constexpr float kLazyRescale = 8.0f;
 
 // D[32x32] += A[32x16] * B[16x32], fp16 inputs, fp32 accumulation.
 // Lane l supplies A[l % 32][8 * (l / 32) + t] and B[8 * (l / 32) + t][l % 32]
@@ -175,6 +179,13 @@ __device__ __forceinline__ float dot2(h2 a, h2 b, float sum) { return __builtin_
 // before a loop, it tells the compiler's wait-count tracking that loads
 // issued earlier need no waits inside the loop.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector memory operations of this wavefront are
+// outstanding (they complete in issue order, so all but the last N issued).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // True on every lane if pred holds on any lane of the wavefront.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }

@@ -63,8 +63,6 @@ struct FwdCfg {
   static_assert(LDS_BYTES <= 65536, "static LDS budget");
 };
 
-// Row-max growth (log2 units) tolerated before the reference max moves.
-constexpr float kLazyRescale = 8.0f;
 
 // Workgroups per CU the register budget is sized for.  Two wavefronts per
 // SIMD let one wavefront's softmax overlap the other's MFMAs: at D <= 128
