@@ -155,13 +155,15 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
 
 // --------------------------------------------------------------- dK and dV
 
-// LDS per stage: Q tile, dO tile (32 x D fp16 each, bswz) and 32 LSE (log2
-// units) + 32 D values.
-template <int D>
+// LDS: the workgroup's V rows (32 NW x D fp16, swz), then per stage a Q
+// tile, a dO tile (32 x D fp16 each, bswz) and 32 LSE (log2 units) + 32 D
+// values.
+template <int D, int NW>
 struct DkdvLds {
+  static constexpr int VROWS = 32 * NW * D * 2;
   static constexpr int TILE = 32 * D * 2;
   static constexpr int STAGE = 2 * TILE + 256;
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int BYTES = VROWS + 2 * STAGE;
 };
 
 template <int D, int NW, bool CAUSAL>
@@ -170,7 +172,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
                 const _Float16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                 _Float16* __restrict__ dK, _Float16* __restrict__ dV, int Sq, int Sk, int BH, int nkt, float scale) {
   using C = BwdCfg<D, NW>;
-  using L = DkdvLds<D>;
+  using L = DkdvLds<D, NW>;
   constexpr int EPI = NW * 32 * D * 2;
   __shared__ __attribute__((aligned(1024))) char smem[(L::BYTES > EPI) ? L::BYTES : EPI];
 
@@ -189,18 +191,18 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
   const u32x4 rq = rsrc_words(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   const u32x4 rdo = rsrc_words(dO + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   const auto rk = make_rsrc(K + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
-  const auto rv = make_rsrc(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
+  const u32x4 rv = rsrc_words(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
   const u32x4 rl = rsrc_words(L2 + (size_t)bh * Sq, (uint32_t)Sq * 4);
   const u32x4 rd = rsrc_words(Dv + (size_t)bh * Sq, (uint32_t)Sq * 4);
 
-  // K and V rows of this wavefront as the B operands of S = Q K^T and
-  // dP = dO V^T: lane l holds d = 16 ks + 8 (l/32) .. +7 of key l%32.
-  h8 kreg[C::KS], vreg[C::KS];
+  // K rows of this wavefront as the B operand of S = Q K^T: lane l holds
+  // d = 16 ks + 8 (l/32) .. +7 of key l%32.  The V rows, the B operand of
+  // dP = dO V^T, are read from LDS in the same pattern (registers are the
+  // scarcer resource here).
+  h8 kreg[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
+  for (int ks = 0; ks < C::KS; ++ks)
     kreg[ks] = as_h8(buf_load16(rk, ((uint32_t)key * D + 16 * ks + 8 * hh) * 2u));
-    vreg[ks] = as_h8(buf_load16(rv, ((uint32_t)key * D + 16 * ks + 8 * hh) * 2u));
-  }
 
   // Query tiles: all of them, or from the diagonal on when causal.
   const int qt0 = CAUSAL ? (k0 / 32) : 0;
@@ -221,8 +223,22 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
     go[u] = (uint32_t)(r * D + c * 8) * 2;
   }
   const uint32_t lds0 = lds_addr_of(smem);
+  // the workgroup's 32 NW V rows, copied once (rows past Sk read as zeros)
+  {
+    constexpr int VBLK = L::VROWS / 1024;
+    static_assert(VBLK % NW == 0, "V rows split");
+#pragma unroll
+    for (int u = 0; u < VBLK / NW; ++u) {
+      const int b = w + u * NW;
+      const int p = b * 1024 + lane * 16;
+      int r, c;
+      swz_inv<C::KCH>(p >> 8, (p >> 4) & 15, r, c);
+      dma16(rv, lds0 + b * 1024, (uint32_t)((k0 + r) * D + c * 8) * 2);
+    }
+  }
+  const char* Vw = smem;  // V rows of this workgroup, [32 NW][D] swz
   auto load_stage = [&](int st, int q0) {
-    const uint32_t base = lds0 + st * L::STAGE;
+    const uint32_t base = lds0 + L::VROWS + st * L::STAGE;
     const uint32_t tb = (uint32_t)q0 * D * 2;
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
@@ -258,7 +274,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
     // while this tile is computed
     if (qt + 1 < nqt) load_stage(st ^ 1, (qt + 1) * 32);
     const int q0 = qt * 32;
-    const char* Qs = smem + st * L::STAGE;
+    const char* Qs = smem + L::VROWS + st * L::STAGE;
     const char* dOs = Qs + L::TILE;
     const float* lv = reinterpret_cast<const float*>(Qs + 2 * L::TILE);
     // a wavefront whose keys all come after the tile's last query sees none
@@ -275,18 +291,26 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
         const h8 aq = *reinterpret_cast<const h8*>(Qs + bswz<C::KCH>(r32, 2 * ks + hh));
         s = mfma_32x32x16(aq, kreg[ks], s);
         const h8 ado = *reinterpret_cast<const h8*>(dOs + bswz<C::KCH>(r32, 2 * ks + hh));
-        dp = mfma_32x32x16(ado, vreg[ks], dp);
+        const h8 bv = *reinterpret_cast<const h8*>(Vw + swz<C::KCH>(32 * w + r32, 2 * ks + hh));
+        dp = mfma_32x32x16(ado, bv, dp);
       }
-      // accumulator j holds query q0 + 8(j/4) + 4 hh + j%4 of key `key`
+      // accumulator j holds query q0 + 8(j/4) + 4 hh + j%4 of key `key`;
+      // masked entries take exp2(-inf) = 0, without a branch
       h8 pop[2], dsop[2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int ql = 8 * (j >> 2) + 4 * hh + (j & 3);
-        const bool keep = (key < Sk) && (q0 + ql < Sq) && (!CAUSAL || key <= q0 + ql);
-        const float p = keep ? exp2_fast(__builtin_fmaf(s[j], c2, -lv[ql])) : 0.f;
-        const float ds = p * (dp[j] - lv[32 + ql]);
-        pop[j >> 3][j & 7] = (_Float16)p;
-        dsop[j >> 3][j & 7] = (_Float16)ds;
+      for (int jg = 0; jg < 4; ++jg) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lv + 8 * jg + 4 * hh);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lv + 32 + 8 * jg + 4 * hh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * jg + i;
+          const int qg = q0 + 8 * jg + 4 * hh + i;
+          const bool keep = (key < Sk) && (qg < Sq) && (!CAUSAL || key <= qg);
+          const float p = exp2_fast(keep ? __builtin_fmaf(s[j], c2, -l4[i]) : kNegInf);
+          const float ds = p * (dp[j] - d4[i]);
+          pop[j >> 3][j & 7] = (_Float16)p;
+          dsop[j >> 3][j & 7] = (_Float16)ds;
+        }
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
@@ -432,7 +456,7 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
         for (int j = 0; j < 16; ++j) {
           const int kk = kt * BN + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
           const bool keep = (kk < Sk) && (!CAUSAL || kk <= qi);
-          const float p = keep ? exp2_fast(__builtin_fmaf(s[kb][j], c2, -lse2)) : 0.f;
+          const float p = exp2_fast(keep ? __builtin_fmaf(s[kb][j], c2, -lse2) : kNegInf);
           dsop[kb][j >> 3][j & 7] = (_Float16)(p * (dp[kb][j] - dval));
         }
 #pragma unroll
