@@ -54,6 +54,8 @@ BRUTE_SHAPES = [
     (1, 2, 9, 4, 3, 0.7),   # more queries than keys (causal rows past Sk see every key)
     (1, 1, 6, 11, 64, 0.125),
     (1, 1, 33, 33, 8, 0.35),
+    (1, 1, 3, 5, 512, 0.05),     # the large head dims of the Split-D path
+    (1, 1, 2, 3, 1024, 0.03125),
 ]
 
 
@@ -174,7 +176,8 @@ def pin_causal_truncation():
 
 def pin_sdpa():
     torch = pytest.importorskip("torch")
-    for (B, H, S, D, sc) in [(2, 3, 17, 16, 0.25), (1, 2, 64, 64, 0.125)]:
+    for (B, H, S, D, sc) in [(2, 3, 17, 16, 0.25), (1, 2, 64, 64, 0.125), (1, 2, 19, 512, 0.05),
+                             (1, 1, 11, 1024, 0.03125)]:
         q = _rand((B, H, S, D), 27)
         k = _rand((B, H, S, D), 28)
         v = _rand((B, H, S, D), 29)
