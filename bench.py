@@ -340,14 +340,17 @@ def main():
         "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
         "traffic": measured_traffic(["fwd_kernel<128,64,causal>"], src_hash),
     }
+    # one partition: a single kernel splits the keys over the 16 wavefronts
+    # of a 1024-thread workgroup and merges them in LDS
+    dec_kernels = ["decode_partial_kernel<128>"] + ([] if ns == 1 else ["decode_merge_kernel<128>"])
     roof_dec = {
-        "kernel": "decode_partial_kernel<128> + decode_merge_kernel<128>",
+        "kernel": "decode_partial_kernel<128,1024,final>" if ns == 1 else " + ".join(dec_kernels),
         "bound": "hbm",
         "achieved": round(gbps, 2),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
         "frac": round(gbps / PEAK_HBM_GBPS, 4),
-        "traffic": measured_traffic(["decode_partial_kernel<128>", "decode_merge_kernel<128>"], src_hash),
+        "traffic": measured_traffic(dec_kernels, src_hash),
     }
     dominant, other = (roof_pre, roof_dec) if t_pre >= t_dec else (roof_dec, roof_pre)
 

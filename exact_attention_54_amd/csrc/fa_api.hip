@@ -155,14 +155,25 @@ int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, floa
   return launched("fa_fwd Split-D merge launch");
 }
 
+// Workgroup size of the single-partition decode (its in-LDS merge writes
+// the final output; no workspace, no merge kernel).
+constexpr int kDecFusedThreads = 1024;
+
 template <int D>
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk,
                   float scale, hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
   const int chunk = (Sk + ns - 1) / ns;
   const float c2 = scale * fa::kLog2e;
-  hipLaunchKernelGGL((fa::decode_partial_kernel<D>), dim3(BH * ns), dim3(fa::DecCfg<D>::THREADS), 0, stream,
+  if (ns == 1) {
+    hipLaunchKernelGGL((fa::decode_partial_kernel<D, kDecFusedThreads, true>), dim3(BH), dim3(kDecFusedThreads), 0,
+                       stream, static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
+                       static_cast<const _Float16*>(v), nullptr, nullptr, static_cast<_Float16*>(o), lse, Sk, 1,
+                       Sk, c2);
+    return launched("decode launch");
+  }
+  hipLaunchKernelGGL((fa::decode_partial_kernel<D, 256, false>), dim3(BH * ns), dim3(256), 0, stream,
                      static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                     static_cast<const _Float16*>(v), ws_o, ws_lse, Sk, ns, chunk, c2);
+                     static_cast<const _Float16*>(v), ws_o, ws_lse, nullptr, nullptr, Sk, ns, chunk, c2);
   int rc = launched("decode phase-one launch");
   if (rc != FA_OK) return rc;
   hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
@@ -176,10 +187,17 @@ int launch_decode_paged(const void* q, const void* kc, const void* vc, const int
                         hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
   const float c2 = scale * fa::kLog2e;
   const int BH = B * H;
-  hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D>), dim3(BH * ns), dim3(fa::DecCfg<D>::THREADS), 0,
-                     stream, static_cast<const _Float16*>(q), static_cast<const _Float16*>(kc),
-                     static_cast<const _Float16*>(vc), tables, seq_lens, ws_o, ws_lse, H, ns, num_blocks, lbs,
-                     max_blocks, c2);
+  if (ns == 1) {
+    hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D, kDecFusedThreads, true>), dim3(BH),
+                       dim3(kDecFusedThreads), 0, stream, static_cast<const _Float16*>(q),
+                       static_cast<const _Float16*>(kc), static_cast<const _Float16*>(vc), tables, seq_lens, nullptr,
+                       nullptr, static_cast<_Float16*>(o), lse, H, 1, num_blocks, lbs, max_blocks, c2);
+    return launched("paged decode launch");
+  }
+  hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D, 256, false>), dim3(BH * ns), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(kc),
+                     static_cast<const _Float16*>(vc), tables, seq_lens, ws_o, ws_lse, nullptr, nullptr, H, ns,
+                     num_blocks, lbs, max_blocks, c2);
   int rc = launched("paged decode phase-one launch");
   if (rc != FA_OK) return rc;
   hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
@@ -331,8 +349,8 @@ int validate_decode(const void* q, const void* k, const void* v, const void* o, 
 
 int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk, int D,
                float scale, hipStream_t stream, int ns, void* ws) {
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o + (size_t)BH * ns * D;
+  float* ws_o = static_cast<float*>(ws);  // unused (may be null) with a single partition
+  float* ws_lse = ws ? ws_o + (size_t)BH * ns * D : nullptr;
   switch (D) {
     case 64: return launch_decode<64>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
     case 128: return launch_decode<128>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
@@ -487,8 +505,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {
   if (B < 1 || H < 1 || Sk < 1 || num_cus < 1) return 0;
-  const int64_t target = (int64_t)8 * num_cus;
   const int64_t bh = (int64_t)B * H;
+  // one 1024-thread workgroup per slice already gives every CU two of them
+  // (32 wavefronts): a single partition, merged in LDS, with no workspace
+  if (bh >= (int64_t)2 * num_cus) return 1;
+  const int64_t target = (int64_t)8 * num_cus;
   int64_t ns = 1;
   while (bh * ns < target && ns < Sk) ns *= 2;
   while (ns > 1 && (Sk + ns - 1) / ns < 256) ns /= 2;
@@ -525,6 +546,7 @@ int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, floa
   rc = resolve_splits(B, H, Sk, num_splits, &ns);
   if (rc != FA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ns == 1) return run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, 1, nullptr);  // no workspace
   hipMemPool_t pool = nullptr;
   rc = workspace_pool(&pool);
   if (rc != FA_OK) return rc;
@@ -547,14 +569,16 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
   rc = resolve_splits(B, H, max_blocks * block_size, num_splits, &ns);
   if (rc != FA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipMemPool_t pool = nullptr;
-  rc = workspace_pool(&pool);
-  if (rc != FA_OK) return rc;
   void* ws = nullptr;
-  rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)B * H, D, ns), pool, s), "workspace allocation");
-  if (rc != FA_OK) return rc;
+  if (ns > 1) {  // a single partition needs no workspace
+    hipMemPool_t pool = nullptr;
+    rc = workspace_pool(&pool);
+    if (rc != FA_OK) return rc;
+    rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)B * H, D, ns), pool, s), "workspace allocation");
+    if (rc != FA_OK) return rc;
+  }
   float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o + (size_t)B * H * ns * D;
+  float* ws_lse = ws ? ws_o + (size_t)B * H * ns * D : nullptr;
   switch (D) {
     case 64:
       rc = launch_decode_paged<64>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
@@ -569,6 +593,7 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
                                     max_blocks, scale, s, ns, ws_o, ws_lse);
       break;
   }
+  if (!ws) return rc;
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
 }

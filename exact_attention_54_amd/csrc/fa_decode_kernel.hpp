@@ -9,21 +9,26 @@
 // bound by HBM bandwidth, not by arithmetic: no MFMA, and the loads are
 // non-temporal.  A key row of D fp16 values is read by LPK = min(16, D/8)
 // lanes with 16-byte loads, so each wavefront instruction moves 64 x 16
-// contiguous bytes (4 key rows at D = 128).  Every lane keeps an independent online softmax over the keys
-// of its slot; the 4 x SLOTS slot states of a workgroup are merged through
-// LDS at the end into one normalised partial output O_s and lse_s.
+// contiguous bytes (4 key rows at D = 128).  Every lane keeps an independent
+// online softmax over the keys of its slot; the NWAVES x SLOTS slot states of
+// a workgroup are merged through LDS at the end into one normalised partial
+// output O_s and lse_s -- the same split-and-merge one level down.
 //
 // Phase two (decode_merge_kernel): per slice, lse = ln sum_s exp(lse_s) and
 // O = sum_s exp(lse_s - lse) O_s, rounded to fp16.
+//
+// With a single partition per slice the workgroup has 1024 threads (16
+// wavefronts, as many as four 256-thread partitions) and its in-LDS merge
+// writes the final fp16 O and LSE: no workspace and no second kernel.
 #pragma once
 
 #include "fa_device.hpp"
 
 namespace fa {
 
-template <int D>
+template <int D, int T = 256>
 struct DecCfg {
-  static constexpr int THREADS = 256;
+  static constexpr int THREADS = T;
   static constexpr int NWAVES = THREADS / 64;
   static constexpr int LPK = (D / 8 < 16) ? D / 8 : 16;  // lanes per key row
   static constexpr int CPL = (D / 8) / LPK;              // 16-byte chunks per lane
@@ -38,14 +43,14 @@ struct DecCfg {
 // wavefront visits (keys base + u * SLOTS + slot, base stepping by the
 // workgroup's stride).  row_of(key) is the element offset of the key's K and
 // V rows, or -1 for a key that is absent (it then scores -inf).
-template <int D, class RowOf>
+template <int D, int T, class RowOf>
 __device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::CPL][8],
                                                   const _Float16* __restrict__ kp,
                                                   const _Float16* __restrict__ vp, int kb, int ke,
                                                   RowOf row_of, int w, int slot, int dl, float c2,
                                                   float& m_run, float& l_run,
                                                   float (&acc)[DecCfg<D>::CPL][8]) {
-  using C = DecCfg<D>;
+  using C = DecCfg<D, T>;
   for (int base = kb + w * C::KEYS_PER_WAVE_ITER; base < ke; base += C::KEYS_PER_WG_ITER) {
     u32x4 kr[C::U][C::CPL], vr[C::U][C::CPL];
     bool present[C::U];
@@ -108,14 +113,16 @@ __device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::C
   }
 }
 
-// Merges the NSTATE slot states of a workgroup through LDS into the
-// normalised partial output out_o[0..D) and its natural-log lse.  A
-// partition whose slots saw no present key gets O_s = 0, lse_s = -inf.
-template <int D>
+// Merges the NSTATE slot states of a workgroup through LDS.  Partial
+// (FINAL false): the normalised partial output out_o[0..D) (fp32) and its
+// natural-log lse; a partition whose slots saw no present key gets O_s = 0,
+// lse_s = -inf.  FINAL: the slice's fp16 output out_h[0..D) and its LSE
+// (O = 0, LSE = -inf when no key is present).
+template <int D, int T, bool FINAL>
 __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, const float (&acc)[DecCfg<D>::CPL][8],
                                                    int tid, int w, int slot, int dl, float* __restrict__ out_o,
-                                                   float* __restrict__ out_lse) {
-  using C = DecCfg<D>;
+                                                   _Float16* __restrict__ out_h, float* __restrict__ out_lse) {
+  using C = DecCfg<D, T>;
   __shared__ float s_m[C::NSTATE];
   __shared__ float s_l[C::NSTATE];
   __shared__ __attribute__((aligned(16))) float s_acc[C::NSTATE][D];
@@ -134,8 +141,11 @@ __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, con
 #pragma unroll
   for (int i = 0; i < C::NSTATE; ++i) M = fmaxf(M, s_m[i]);
   for (int d = tid; d < D; d += C::THREADS) {
-    if (M == kNegInf) {  // no present key in the partition
-      out_o[d] = 0.f;
+    if (M == kNegInf) {  // no present key
+      if constexpr (FINAL)
+        out_h[d] = (_Float16)0.f;
+      else
+        out_o[d] = 0.f;
       if (d == 0) *out_lse = kNegInf;
       continue;
     }
@@ -146,18 +156,23 @@ __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, con
       den += wgt * s_l[i];
       num += wgt * s_acc[i][d];
     }
-    out_o[d] = num / den;
+    if constexpr (FINAL)
+      out_h[d] = (_Float16)(num / den);
+    else
+      out_o[d] = num / den;
     if (d == 0) *out_lse = (M + __builtin_log2f(den)) * kLn2;
   }
 }
 
-// ws_o: [BH, ns, D] fp32, ws_lse: [BH, ns] fp32 (natural log).
-template <int D>
-__global__ void __launch_bounds__(256)
+// Partial (FINAL false): ws_o [BH, ns, D] fp32, ws_lse [BH, ns] fp32
+// (natural log).  FINAL (ns = 1): O [BH, D] fp16 and LSE [BH] directly.
+template <int D, int T, bool FINAL>
+__global__ void __launch_bounds__(T)
 decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                       const _Float16* __restrict__ V, float* __restrict__ ws_o,
-                      float* __restrict__ ws_lse, int Sk, int ns, int chunk, float c2) {
-  using C = DecCfg<D>;
+                      float* __restrict__ ws_lse, _Float16* __restrict__ O, float* __restrict__ LSE, int Sk,
+                      int ns, int chunk, float c2) {
+  using C = DecCfg<D, T>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -167,11 +182,18 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
   const int s = blockIdx.x - bh * ns;
   const int k0 = s * chunk;
   const int k1 = min(Sk, k0 + chunk);
-  float* out_o = ws_o + ((size_t)bh * ns + s) * D;
+  float* out_o = FINAL ? nullptr : ws_o + ((size_t)bh * ns + s) * D;
+  _Float16* out_h = FINAL ? O + (size_t)bh * D : nullptr;
+  float* out_lse = FINAL ? LSE + bh : ws_lse + (size_t)bh * ns + s;
 
   if (k0 >= k1) {  // empty partition: weight zero in the merge
-    for (int d = tid; d < D; d += C::THREADS) out_o[d] = 0.f;
-    if (tid == 0) ws_lse[(size_t)bh * ns + s] = kNegInf;
+    for (int d = tid; d < D; d += C::THREADS) {
+      if constexpr (FINAL)
+        out_h[d] = (_Float16)0.f;
+      else
+        out_o[d] = 0.f;
+    }
+    if (tid == 0) *out_lse = kNegInf;
     return;
   }
 
@@ -191,9 +213,9 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
 
-  decode_accumulate<D>(qf, K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, k0, k1,
-                       [](int key) { return (int64_t)key; }, w, slot, dl, c2, m_run, l_run, acc);
-  decode_merge_slots<D>(m_run, l_run, acc, tid, w, slot, dl, out_o, ws_lse + (size_t)bh * ns + s);
+  decode_accumulate<D, T>(qf, K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, k0, k1,
+                          [](int key) { return (int64_t)key; }, w, slot, dl, c2, m_run, l_run, acc);
+  decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
 
 // Paged KV cache ("Adaptive High-Performance Attention Kernels in CUDA",
@@ -207,14 +229,14 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 // entries outside [0, num_blocks) mark absent keys: they are never read.
 constexpr int kPagedTbl = 1024;
 
-template <int D>
-__global__ void __launch_bounds__(256)
+template <int D, int T, bool FINAL>
+__global__ void __launch_bounds__(T)
 decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ Kc,
                             const _Float16* __restrict__ Vc, const int* __restrict__ tables,
                             const int* __restrict__ seq_lens, float* __restrict__ ws_o,
-                            float* __restrict__ ws_lse, int H, int ns, int num_blocks, int lbs,
-                            int max_blocks, float c2) {
-  using C = DecCfg<D>;
+                            float* __restrict__ ws_lse, _Float16* __restrict__ O, float* __restrict__ LSE, int H,
+                            int ns, int num_blocks, int lbs, int max_blocks, float c2) {
+  using C = DecCfg<D, T>;
   __shared__ int s_tbl[kPagedTbl];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -230,11 +252,18 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
   const int chunk = (L + ns - 1) / ns;
   const int k0 = s * chunk;
   const int k1 = min(L, k0 + chunk);
-  float* out_o = ws_o + ((size_t)bh * ns + s) * D;
+  float* out_o = FINAL ? nullptr : ws_o + ((size_t)bh * ns + s) * D;
+  _Float16* out_h = FINAL ? O + (size_t)bh * D : nullptr;
+  float* out_lse = FINAL ? LSE + bh : ws_lse + (size_t)bh * ns + s;
 
   if (k0 >= k1) {  // empty partition (or empty context): weight zero in the merge
-    for (int d = tid; d < D; d += C::THREADS) out_o[d] = 0.f;
-    if (tid == 0) ws_lse[(size_t)bh * ns + s] = kNegInf;
+    for (int d = tid; d < D; d += C::THREADS) {
+      if constexpr (FINAL)
+        out_h[d] = (_Float16)0.f;
+      else
+        out_o[d] = 0.f;
+    }
+    if (tid == 0) *out_lse = kNegInf;
     return;
   }
 
@@ -264,7 +293,7 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
     __syncthreads();  // the previous segment's table reads are done
     for (int i = tid; i < nblk; i += C::THREADS) s_tbl[i] = trow[blk0 + i];
     __syncthreads();
-    decode_accumulate<D>(
+    decode_accumulate<D, T>(
         qf, Kc, Vc, seg, seg_end,
         [&](int key) -> int64_t {
           const int pb = s_tbl[(key >> lbs) - blk0];
@@ -273,7 +302,7 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
         },
         w, slot, dl, c2, m_run, l_run, acc);
   }
-  decode_merge_slots<D>(m_run, l_run, acc, tid, w, slot, dl, out_o, ws_lse + (size_t)bh * ns + s);
+  decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
 
 template <int D>

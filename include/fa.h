@@ -150,9 +150,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * [s*c, min((s+1)*c, Sk)) with c = ceil(Sk / num_splits); trailing
  * partitions may be empty.  num_splits <= 0 picks fa_decode_auto_splits()
  * for the current device; otherwise 1 <= num_splits <= Sk.
- * Phase one writes a normalised partial output and its LSE per partition;
- * phase two merges them with log-sum-exp weights into o and lse.  Both
- * kernels run on `stream`.  The partials live in a workspace taken from a
+ * With one partition (num_splits == 1), one 1024-thread workgroup per
+ * (batch, head) splits the keys over its 16 wavefronts, merges their
+ * partial states in LDS with the same log-sum-exp weights and writes o and
+ * lse: one kernel, no workspace.  Otherwise phase one writes a normalised
+ * partial output and its LSE per partition, and phase two merges them with
+ * log-sum-exp weights into o and lse.  Both kernels run on `stream`.  The partials live in a workspace taken from a
  * per-device memory pool that the library creates on first use (stream-
  * ordered hipMallocFromPoolAsync / hipFreeAsync on `stream`, so nothing
  * blocks); the pool keeps freed memory for reuse until the process ends.
@@ -175,8 +178,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits);
  * aligned, where ns is the resolved split count).  Nothing is allocated.
  * On return the workspace is laid out as partial outputs fp32
  * [B, H, ns, D] followed by partial LSEs fp32 [B, H, ns] (natural log;
- * -inf for an empty partition, whose partial output is 0).  Calls that
- * share one workspace must be ordered on one stream.
+ * -inf for an empty partition, whose partial output is 0).  With ns == 1
+ * the workspace is checked but not touched.  Calls that share one
+ * workspace must be ordered on one stream.
  */
 int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int H, int Sq, int Sk, int D, int causal, float scale,
@@ -215,10 +219,11 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 
 /*
  * fa_decode_auto_splits -- the split count fa_decode_splitkv uses when
- * num_splits <= 0: the smallest power of two that gives at least
- * 8 * num_cus phase-one workgroups, lowered until every partition holds at
- * least 256 keys (never below 1, never above Sk).  Pure host arithmetic;
- * returns 0 for invalid sizes.
+ * num_splits <= 0: 1 when B*H >= 2 * num_cus (one 1024-thread workgroup
+ * per slice then gives every CU two); otherwise the smallest power of two
+ * that gives at least 8 * num_cus 256-thread phase-one workgroups, lowered
+ * until every partition holds at least 256 keys (never below 1, never above
+ * Sk).  Pure host arithmetic; returns 0 for invalid sizes.
  */
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
 

@@ -131,11 +131,12 @@ def test_workspace_bytes(lib):
 
 
 @pytest.mark.parametrize("B,H,Sk,cus,want", [
-    (16, 32, 8192, 256, 4),     # 512 slices x 4 = 2048 workgroups = 8 per CU
+    (16, 32, 8192, 256, 1),     # 512 slices: two 1024-thread workgroups per CU, no split
+    (8, 32, 8192, 256, 8),      # 256 slices x 8 = 2048 workgroups of 256 threads = 8 per CU
     (1, 1, 8192, 256, 32),      # capped so each partition keeps >= 256 keys
     (1, 1, 100, 256, 1),
     (1, 1, 1, 256, 1),
-    (64, 64, 8192, 256, 1),     # already 16 workgroups per CU
+    (64, 64, 8192, 256, 1),     # already 16 slices per CU
     (2, 8, 4096, 304, 16),
     (0, 1, 10, 256, 0),
     (1, 1, 10, 0, 0),
