@@ -42,10 +42,16 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: // comments, trailing blanks and
+    empty lines are left out, so that a comment edit keeps the stored
+    counter figures valid while any code change retires them."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_attention_54_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_54_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -294,9 +294,14 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
         const h8 bv = *reinterpret_cast<const h8*>(Vw + swz<C::KCH>(32 * w + r32, 2 * ks + hh));
         dp = mfma_32x32x16(ado, bv, dp);
       }
-      // accumulator j holds query q0 + 8(j/4) + 4 hh + j%4 of key `key`;
-      // masked entries take exp2(-inf) = 0, without a branch
+      // accumulator j holds query q0 + 4 hh + c, c = 8(j/4) + j%4, of key
+      // `key`; it is kept for lo <= c < hi (key < Sk, query < Sq, and
+      // key <= query when causal), one unsigned compare against a constant.
+      // Masked entries take exp2(-inf) = 0, without a branch.
       h8 pop[2], dsop[2];
+      const int lo = CAUSAL ? max(key - q0 - 4 * hh, 0) : 0;
+      const int hi = (key < Sk) ? max(min(Sq - q0 - 4 * hh, 32), lo) : lo;
+      const unsigned span = (unsigned)(hi - lo);
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lv + 8 * jg + 4 * hh);
@@ -304,8 +309,7 @@ bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * jg + i;
-          const int qg = q0 + 8 * jg + 4 * hh + i;
-          const bool keep = (key < Sk) && (qg < Sq) && (!CAUSAL || key <= qg);
+          const bool keep = (unsigned)(8 * jg + i - lo) < span;
           const float p = exp2_fast(keep ? __builtin_fmaf(s[j], c2, -l4[i]) : kNegInf);
           const float ds = p * (dp[j] - d4[i]);
           pop[j >> 3][j & 7] = (_Float16)p;
@@ -448,14 +452,17 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
           dp[kb] = mfma_32x32x16(av, doreg[ks], dp[kb]);
         }
       }
-      // accumulator j of block kb holds key kt*BN + 32 kb + 8(j/4) + 4 hh + j%4
+      // accumulator j of block kb holds key kt*BN + 4 hh + c with
+      // c = 32 kb + 8(j/4) + j%4; it is kept for c <= lim (key < Sk, and
+      // key <= query when causal): one compare against a constant
       h8 dsop[NKB][2];
+      const int kbase = kt * BN + 4 * hh;
+      const int lim = CAUSAL ? min(Sk - 1, qi) - kbase : Sk - 1 - kbase;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int kk = kt * BN + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-          const bool keep = (kk < Sk) && (!CAUSAL || kk <= qi);
+          const bool keep = 32 * kb + 8 * (j >> 2) + (j & 3) <= lim;
           const float p = exp2_fast(keep ? __builtin_fmaf(s[kb][j], c2, -lse2) : kNegInf);
           dsop[kb][j >> 3][j & 7] = (_Float16)(p * (dp[kb][j] - dval));
         }

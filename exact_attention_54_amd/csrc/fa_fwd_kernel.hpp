@@ -17,8 +17,9 @@
 //                 ("FlashAttention-2 MMA", Technical Details, Online Softmax).
 //                 The reference max m only moves when a row max grows by
 //                 more than 2^8 (then O and l are rescaled by 2^(m - m_new));
-//                 in between p <= 2^8, which fp16 and fp32 hold exactly, so
-//                 the result is unchanged and the rescale is rare.
+//                 in between p <= 2^8, well inside fp16's range and at its
+//                 full relative precision, so only rounding differs and the
+//                 rescale is rare.
 //   O^T += V^T P^T  P is rounded to fp16 in registers and used directly as
 //                 the B operand: the accumulator layout of S^T lists keys
 //                 8*(j/4) + 4*(l/32) + j%4, and the contraction index is
