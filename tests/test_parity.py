@@ -230,6 +230,21 @@ def test_decode_partials_match_oracle(torch_dev, fa):
     assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, "decode merged via _ws")
 
 
+def test_decode_single_partition_leaves_workspace_alone(torch_dev, fa):
+    # one partition: one kernel merges in LDS and writes o and lse directly
+    torch, dev = torch_dev
+    B, H, Sk, D = 2, 3, 777, 128
+    q, k, v = make_qkv(B, H, 1, Sk, D, seed=43)
+    nbytes = fa.fa_decode_workspace_bytes(B, H, D, 1)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=dev)
+    qd, kd, vd = to_dev(torch_dev, q, k, v)
+    o, lse = fa.fa_decode_splitkv_ws(qd, kd, vd, ws, scale=0.125, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.isnan(ws).all()
+    O, L = oracle.attention(q, k, v, False, 0.125)
+    assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, "decode ns=1 via _ws")
+
+
 # ------------------------------------------------- determinism and errors
 
 def test_run_to_run_bitwise(torch_dev, fa):

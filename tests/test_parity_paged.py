@@ -101,7 +101,8 @@ def test_paged_long_partition_segments(torch_dev, fa):
     check(o, lse, O, L, "segments")
 
 
-def test_paged_absent_and_out_of_range_pages(torch_dev, fa):
+@pytest.mark.parametrize("ns", [0, 1, 3])   # 1: the single-kernel form merges in LDS
+def test_paged_absent_and_out_of_range_pages(torch_dev, fa, ns):
     B, H, S, D, bs = 3, 2, 96, 64, 16
     q, kc, vc, tables = case(B, H, S, D, bs, 41)
     tables = tables.copy()
@@ -109,19 +110,20 @@ def test_paged_absent_and_out_of_range_pages(torch_dev, fa):
     tables[1, 0] = kc.shape[0]       # one past the last page
     tables[2, :] = 2 ** 30           # every page of sequence 2 absent -> empty
     seq_lens = np.array([96, 80, 96], dtype=np.int32)
-    o, lse = gpu_paged(torch_dev, fa, q, kc, vc, tables, seq_lens, 0.125, 0)
+    o, lse = gpu_paged(torch_dev, fa, q, kc, vc, tables, seq_lens, 0.125, ns)
     O, L = oracle.decode_paged(q, kc, vc, tables, seq_lens, 0.125)
-    check(o, lse, O, L, "absent pages")
+    check(o, lse, O, L, f"absent pages ns={ns}")
     assert (o[2] == 0).all() and np.isneginf(lse[2]).all()
 
 
-def test_paged_empty_and_clamped_contexts(torch_dev, fa):
+@pytest.mark.parametrize("ns", [1, 3])
+def test_paged_empty_and_clamped_contexts(torch_dev, fa, ns):
     B, H, S, D, bs = 4, 2, 48, 128, 16
     q, kc, vc, tables = case(B, H, S, D, bs, 51)
     seq_lens = np.array([0, -7, 10 ** 6, 48], dtype=np.int32)
-    o, lse = gpu_paged(torch_dev, fa, q, kc, vc, tables, seq_lens, 0.2, 3)
+    o, lse = gpu_paged(torch_dev, fa, q, kc, vc, tables, seq_lens, 0.2, ns)
     O, L = oracle.decode_paged(q, kc, vc, tables, seq_lens, 0.2)
-    check(o, lse, O, L, "empty / clamped")
+    check(o, lse, O, L, f"empty / clamped ns={ns}")
     assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
 
 
