@@ -80,8 +80,12 @@ enum fa_status {
  * above the diagonal are never loaded (same page, Lever A).  Head dims 512
  * and 1024 take the Split-D kernel (same strategy list, 3. Split-D): the
  * D/128 wavefronts of a workgroup share 32 query rows, each owns a 128-wide
- * slice of D, and their partial scores are summed through LDS.  Any Sq
- * works, including Sq = 1.  o and lse must not overlap the inputs.
+ * slice of D, and their partial scores are summed through LDS.  When those
+ * (query tile, slice) work items are fewer than the CUs, the Split-D key
+ * range is also split and the parts merged with log-sum-exp weights
+ * ("Split-KV" of the same list); their fp32 partials then live in a
+ * workspace from the library's stream-ordered pool (see fa_decode_splitkv).
+ * Any Sq works, including Sq = 1.  o and lse must not overlap the inputs.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Sq, int Sk, int D, int causal, float scale,
