@@ -314,8 +314,41 @@ def main():
     log(f"backward (causal prefill shape): {t_bwd * 1e6:.1f} us = {tflops_bwd:.1f} TFLOPS (2.5 x forward FLOPs)")
     del dq3, dk3, dv3, do3
 
-    # Split-D forward on the large-head shapes (D = 512 and 1024), both masks,
-    # timed back to back; FLOPs counted as for the prefill above.
+    # The D = 256 causal prefill (1,16,2048,2048,256) and the Split-D forward
+    # on the large-head shapes (D = 512 and 1024), both masks, timed back to
+    # back; FLOPs counted as for the prefill above.
+    w5 = WORKLOADS["d256_prefill"]
+    q5, k5, v5 = (torch.from_numpy(x).to(dev) for x in workload_inputs(w5))
+    o5 = torch.empty_like(q5)
+    l5 = torch.empty((w5.B, w5.H, w5.Sq), dtype=torch.float32, device=dev)
+
+    def d256():
+        fa.fa_fwd(q5, k5, v5, o5, l5, causal=True, scale=w5.scale)
+
+    for _ in range(args.warmup):
+        d256()
+    t_d256 = time_launches(torch, d256, args.steps)
+    tflops_d256 = prefill_flops(w5.B, w5.H, w5.Sq, w5.Sk, w5.D, True) / t_d256 / 1e12
+    log(f"D=256 causal prefill (1,16,2048,2048,256): {t_d256 * 1e6:.1f} us = {tflops_d256:.1f} TFLOPS")
+    del q5, k5, v5, o5, l5
+    # the small (8,16,256,256,64) shape, both masks: launch-sized work
+    w2 = WORKLOADS["small"]
+    q2, k2, v2 = (torch.from_numpy(x).to(dev) for x in workload_inputs(w2))
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty((w2.B, w2.H, w2.Sq), dtype=torch.float32, device=dev)
+    small = {}
+    for causal in (False, True):
+        def small_fwd():
+            fa.fa_fwd(q2, k2, v2, o2, l2, causal=causal, scale=w2.scale)
+
+        for _ in range(args.warmup):
+            small_fwd()
+        t = time_launches(torch, small_fwd, args.steps)
+        tag = "small_prefill_" + ("causal" if causal else "full")
+        small[tag + "_us"] = round(t * 1e6, 2)
+        small[tag + "_tflops"] = round(prefill_flops(w2.B, w2.H, w2.Sq, w2.Sk, w2.D, causal) / t / 1e12, 3)
+        log(f"small (8,16,256,256,64) causal={causal}: {t * 1e6:.1f} us per call")
+    del q2, k2, v2, o2, l2
     splitd = {}
     for name in ("d512_prefill", "d1024_prefill"):
         w = WORKLOADS[name]
@@ -395,6 +428,10 @@ def main():
             "backward_tflops": round(tflops_bwd, 3),
             "backward_frac_of_peak": round(tflops_bwd / PEAK_FP16_TFLOPS, 4),
             "backward_us": round(t_bwd * 1e6, 2),
+            "d256_prefill_tflops": round(tflops_d256, 3),
+            "d256_prefill_frac_of_peak": round(tflops_d256 / PEAK_FP16_TFLOPS, 4),
+            "d256_prefill_us": round(t_d256 * 1e6, 2),
+            **small,
             **{"splitd_" + k: x for k, x in splitd.items()},
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,
