@@ -91,6 +91,34 @@ def time_launches(torch, fn, n):
     return start.elapsed_time(end) / n * 1e-3  # seconds
 
 
+def roofline_context(torch, dev, buf, cus, warmup):
+    """Times the plain read-stream and MFMA-loop probes (HIP events)."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hip", "libroofline_probe.so"))
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    st = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = buf.numel() * buf.element_size()
+    rblocks, mblocks, iters = 16 * cus, 2 * cus, 4096
+    sink = torch.empty(max(rblocks, mblocks) * 256, dtype=torch.float32, device=dev)
+
+    def read():
+        assert lib.probe_stream_read(buf.data_ptr(), nbytes, rblocks, sink.data_ptr(), st) == 0
+
+    def mfma():
+        assert lib.probe_mfma_loop(mblocks, iters, sink.data_ptr(), st) == 0
+
+    for _ in range(max(warmup, 3)):
+        read()
+        mfma()
+    t_read = time_launches(torch, read, 10)
+    t_mfma = time_launches(torch, mfma, 10)
+    mfma_flops = mblocks * 4 * iters * 8 * 32768.0   # 4 wavefronts per block, 8 MFMAs per round
+    return {"context_stream_read_gbps": round(nbytes / t_read / 1e9, 1),
+            "context_mfma_loop_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -369,6 +397,13 @@ def main():
             log(f"split-D {name} causal={causal}: {t * 1e6:.1f} us = {tf:.1f} TFLOPS")
         del qx, kx, vx, ox, lx
 
+    # Context, not the metric: what a plain 16-byte non-temporal read stream
+    # (over the 1 GiB K cache) and a plain register-only fp16 MFMA loop reach
+    # on this GPU right now (tests/hip/roofline_probe.hip).
+    context = roofline_context(torch, dev, k4, cus, args.warmup)
+    log(f"context: plain HBM read stream {context['context_stream_read_gbps']:.1f} GB/s; "
+        f"plain fp16 MFMA loop {context['context_mfma_loop_tflops']:.1f} TFLOPS")
+
     src_hash = kernel_source_hash()
     roof_pre = {
         "kernel": "fwd_kernel<128,64,causal>",
@@ -432,6 +467,7 @@ def main():
             "d256_prefill_frac_of_peak": round(tflops_d256 / PEAK_FP16_TFLOPS, 4),
             "d256_prefill_us": round(t_d256 * 1e6, 2),
             **small,
+            **context,
             **{"splitd_" + k: x for k, x in splitd.items()},
             "accumulate": "fp32",
             "kernel_source_hash": src_hash,

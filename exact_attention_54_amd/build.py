@@ -3,8 +3,10 @@
     python -m exact_attention_54_amd.build        # or __graft_entry__.build()
 
 Produces ``exact_attention_54_amd/libfa_hip.so`` from ``csrc/fa_api.hip``
-(the C ABI of ``include/fa.h`` plus every kernel) and the test-only MFMA
-layout probe ``tests/hip/libmfma_probe.so``.  Always recompiles.
+(the C ABI of ``include/fa.h`` plus every kernel), the test-only MFMA
+layout probe ``tests/hip/libmfma_probe.so`` and the streaming-read / MFMA
+loop probes ``tests/hip/libroofline_probe.so`` that bench.py reports as
+context.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -72,8 +74,17 @@ def build_test_probe(verbose: bool = False) -> str:
     return compile_shared([PROBE_SRC], PROBE_LIB, verbose=verbose)
 
 
+ROOFLINE_SRC = os.path.join(ROOT, "tests", "hip", "roofline_probe.hip")
+ROOFLINE_LIB = os.path.join(ROOT, "tests", "hip", "libroofline_probe.so")
+
+
+def build_roofline_probe(verbose: bool = False) -> str:
+    """Plain HBM-read and MFMA-loop kernels that bench.py times for context."""
+    return compile_shared([ROOFLINE_SRC], ROOFLINE_LIB, verbose=verbose)
+
+
 def build_all(verbose: bool = False):
-    return [build_library(verbose), build_test_probe(verbose)]
+    return [build_library(verbose), build_test_probe(verbose), build_roofline_probe(verbose)]
 
 
 if __name__ == "__main__":

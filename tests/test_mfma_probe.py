@@ -66,3 +66,27 @@ def test_permlane32_swap_exchanges_wave_halves():
     xs = list(range(1000, 1064))
     assert lo.cpu().tolist() == xs[:32] + xs[:32]
     assert hi.cpu().tolist() == xs[32:] + xs[32:]
+
+
+ROOFLINE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libroofline_probe.so")
+
+
+def test_roofline_probes_run():
+    # the context probes bench.py times: a read stream over a known buffer
+    # (every thread's fold lands in the sink) and a short MFMA loop
+    import torch
+
+    assert os.path.exists(ROOFLINE), "roofline probe library not built"
+    lib = ctypes.CDLL(ROOFLINE)
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    sink = torch.full((4 * 256,), -1.0, dtype=torch.float32, device=dev)
+    assert lib.probe_stream_read(buf.data_ptr(), buf.numel() * 4, 4, sink.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert (sink == 0).all()  # XOR of zeros
+    assert lib.probe_stream_read(buf.data_ptr(), 10, 4, sink.data_ptr(), None) == 1  # not a multiple of 16
+    assert lib.probe_mfma_loop(4, 3, sink.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
