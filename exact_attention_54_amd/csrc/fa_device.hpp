@@ -109,26 +109,24 @@ __device__ __forceinline__ h4v lds_read_tr16(const char* p) {
   return __builtin_bit_cast(h4v, v);
 }
 
-// 16-byte global -> LDS copy per lane through a buffer resource.  The LDS
-// destination of lane l is lds_base + 16 l (lds_base is wave-uniform); a
-// load past the buffer's end writes zeros.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0, 0);
-}
-
-// The same copy issued from inline asm, for loops that order the copies
-// themselves: the compiler then does not count them as pending LDS writes
-// (it would wait for all of them before every LDS read it cannot tell
-// apart), so the caller waits with s_waitcnt vmcnt before the barrier that
-// publishes the data.  rs: the four descriptor dwords; lds_addr: the
-// wave-uniform LDS byte address (M0) that lane l's 16 (dma16) or 4 (dma4)
-// bytes land at plus 16 l (4 l).
+// Direct global -> LDS copies through a buffer resource (a load past the
+// buffer's end writes zeros), issued from inline asm: the compiler then
+// does not count them as pending LDS writes.  Issued through the builtin it
+// waits for every outstanding copy before each LDS read it cannot tell
+// apart from their destinations (the transposed V reads of the prefill
+// among them), which cut the prefetch distance to a fraction of a tile; the
+// kernels order the copies themselves and wait with s_waitcnt vmcnt before
+// the barrier that publishes the data.  rs: the four descriptor dwords;
+// lds_addr: the wave-uniform LDS byte address (M0) that lane l's 16 (dma16)
+// or 4 (dma4) bytes land at plus 16 l (4 l).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
   u32x4 r;
-  r[0] = (uint32_t)a;
-  r[1] = (uint32_t)(a >> 32) & 0xffffu;
-  r[2] = bytes;
+  // the descriptor goes to scalar registers; the values are uniform, and
+  // readfirstlane lets the compiler place them there in every caller
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
   r[3] = 0x00020000u;
   return r;
 }

@@ -153,8 +153,6 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // past Sq are dropped (the extent ends with the last row's D elements).
   auto extent = [&](int rows) { return rows > 0 ? (uint32_t)((rows - 1) * RS + D) * 2u : 0u; };
   const auto rq = make_rsrc(qs, extent(Sq));
-  const auto rk = make_rsrc(ks_, extent(Sk));
-  const auto rv = make_rsrc(vs, extent(Sk));
   const auto ro = make_rsrc(os, extent(Sq));
 
   // Q fragment: B operand of S^T = K Q^T, 8 consecutive d per lane and step.
@@ -182,17 +180,20 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     vgo[u] = (uint32_t)(r * RS + c * 8) * 2;
   }
   const uint32_t tile_stride = (uint32_t)BN * RS * 2;  // bytes between key tiles
+  const u32x4 rkw = rsrc_words(ks_, extent(Sk));
+  const u32x4 rvw = rsrc_words(vs, extent(Sk));
+  const uint32_t lds0 = lds_addr_of(smem);
   auto load_k = [&](int kt, int stage) {
     const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u)
-      buf_load16_lds(rk, smem + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + kgo[u]);
+      dma16(rkw, lds0 + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + kgo[u]);
   };
   auto load_v = [&](int kt, int stage) {
     const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u)
-      buf_load16_lds(rv, smem + C::V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
+      dma16(rvw, lds0 + C::V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
   };
 
   // S^T = K Q^T for the tile in K stage `stage`.
