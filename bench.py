@@ -42,10 +42,14 @@ def log(msg):
 
 
 def kernel_source_hash():
-    """Hash of the kernel sources' code: // comments, trailing blanks and
-    empty lines are left out, so that a comment edit keeps the stored
-    counter figures valid while any code change retires them."""
+    """Hash of the kernel sources' code and the library's compiler flags: //
+    comments, trailing blanks and empty lines are left out, so that a
+    comment edit keeps the stored counter figures valid while any code or
+    flag change retires them."""
+    from exact_attention_54_amd import build as fa_build
+
     h = hashlib.sha256()
+    h.update(repr(fa_build.COMMON_FLAGS + fa_build.LIB_FLAGS).encode())
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "exact_attention_54_amd", "csrc", name), encoding="utf-8") as f:
             for line in f:

@@ -65,8 +65,15 @@ PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
 
 
+# The compiler's iterative ILP scheduler orders the prefill's MFMA, exp and
+# LDS work better than the default (3% on the LLaMA-shaped prefill, 1% on
+# the backward, 3% slower on the D = 512 Split-D forward; all bit-identical).
+LIB_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+
+
 def build_library(verbose: bool = False) -> str:
-    return compile_shared([os.path.join(CSRC, "fa_api.hip")], LIB, include_dirs=[INCLUDE, CSRC], verbose=verbose)
+    return compile_shared([os.path.join(CSRC, "fa_api.hip")], LIB, include_dirs=[INCLUDE, CSRC], extra=LIB_FLAGS,
+                          verbose=verbose)
 
 
 def build_test_probe(verbose: bool = False) -> str:
