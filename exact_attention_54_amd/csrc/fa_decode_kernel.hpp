@@ -138,7 +138,7 @@ __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, con
   __syncthreads();
 
   float M = kNegInf;
-#pragma unroll
+#pragma unroll 8
   for (int i = 0; i < C::NSTATE; ++i) M = fmaxf(M, s_m[i]);
   for (int d = tid; d < D; d += C::THREADS) {
     if (M == kNegInf) {  // no present key
@@ -150,7 +150,7 @@ __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, con
       continue;
     }
     float den = 0.f, num = 0.f;
-#pragma unroll
+#pragma unroll 8
     for (int i = 0; i < C::NSTATE; ++i) {
       const float wgt = exp2_fast(s_m[i] - M);  // 0 for a slot that saw no key
       den += wgt * s_l[i];
@@ -166,8 +166,14 @@ __device__ __forceinline__ void decode_merge_slots(float m_run, float l_run, con
 
 // Partial (FINAL false): ws_o [BH, ns, D] fp32, ws_lse [BH, ns] fp32
 // (natural log).  FINAL (ns = 1): O [BH, D] fp16 and LSE [BH] directly.
+// Occupancy target of the contiguous kernel: 8 wavefronts per SIMD (two
+// 1024-thread or eight 256-thread workgroups per CU) at D <= 128, 4 at
+// D = 256.
+template <int D>
+constexpr int dec_waves_per_eu() { return D <= 128 ? 8 : 4; }
+
 template <int D, int T, bool FINAL>
-__global__ void __launch_bounds__(T)
+__global__ void __launch_bounds__(T, dec_waves_per_eu<D>())
 decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                       const _Float16* __restrict__ V, float* __restrict__ ws_o,
                       float* __restrict__ ws_lse, _Float16* __restrict__ O, float* __restrict__ LSE, int Sk,
@@ -229,6 +235,8 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 // entries outside [0, num_blocks) mark absent keys: they are never read.
 constexpr int kPagedTbl = 1024;
 
+// (no occupancy target: held to 64 registers the page translation spills,
+// which measured 7% slower than one 1024-thread workgroup per CU)
 template <int D, int T, bool FINAL>
 __global__ void __launch_bounds__(T)
 decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ Kc,
