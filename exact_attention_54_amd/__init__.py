@@ -171,7 +171,13 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
 
 
 def fa_decode_splitkv(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None, num_splits=0):
-    """Split-KV single-query decoding; returns (o, lse).  num_splits <= 0 = auto."""
+    """Split-KV single-query decoding; returns (o, lse).
+
+    num_splits <= 0 picks the split count automatically; 1 runs one kernel
+    whose 16 wavefronts per (batch, head) split the keys and merge in LDS
+    (no workspace); more partitions write partials that a merge kernel
+    combines.  See fa_decode_splitkv in include/fa.h.
+    """
     B, H, Sq, Sk, D = _check_qkv(q, k, v)
     o, lse = _outputs(q, o, lse)
     if scale is None:
