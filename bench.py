@@ -82,10 +82,61 @@ def prefill_flops(B, H, Sq, Sk, D, causal):
     return f / 2 if causal else f
 
 
+_HIP = None
+
+
+def _hip_runtime():
+    """The HIP runtime this process already runs on (torch's copy)."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), "libamdhip64.so")
+        lib = ctypes.CDLL(path)
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = lib
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP event for timing only, recorded on torch's current stream (the
+    stream the library launches on).  It is created with
+    hipEventDisableSystemFence: recording it performs no system-scope memory
+    fence, so timed kernels are not separated by L2 write-backs and
+    invalidations, as they are by torch.cuda.Event's default events.  The
+    elapsed times are read after torch.cuda.synchronize()."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch):
+        import ctypes
+
+        self._ct = ctypes
+        self.hip = _hip_runtime()
+        self.ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS) == 0
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def record(self):
+        assert self.hip.hipEventRecord(self.ev, self.stream) == 0
+
+    def elapsed_time(self, end):
+        t = self._ct.c_float()
+        assert self.hip.hipEventElapsedTime(self._ct.byref(t), self.ev, end.ev) == 0
+        return t.value
+
+    def __del__(self):
+        if getattr(self, "ev", None):
+            self.hip.hipEventDestroy(self.ev)
+
+
 def time_launches(torch, fn, n):
-    """Average duration of one call of fn, HIP events on the current stream."""
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    """Average duration of one call of fn, HIP timing events on the current stream."""
+    start = TimingEvent(torch)
+    end = TimingEvent(torch)
     torch.cuda.synchronize()
     start.record()
     for _ in range(n):
@@ -244,9 +295,9 @@ def main():
     log(f"timing {args.steps} steps")
     # events around every launch inside the timed loop: the per-kernel
     # averages are taken under the same conditions as the step time
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ev = [[TimingEvent(torch) for _ in range(3)] for _ in range(args.steps)]
+    start = TimingEvent(torch)
+    end = TimingEvent(torch)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
