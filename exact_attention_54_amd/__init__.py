@@ -27,6 +27,7 @@ __all__ = [
     "fa_decode_paged",
     "fa_decode_workspace_bytes",
     "fa_decode_auto_splits",
+    "fa_fwd_key_splits",
     "fa_status_string",
     "fa_last_error",
     "FAError",
@@ -251,6 +252,11 @@ def fa_decode_workspace_bytes(B, H, D, num_splits):
 
 def fa_decode_auto_splits(B, H, Sk, num_cus):
     return int(_capi.load().fa_decode_auto_splits(B, H, Sk, num_cus))
+
+
+def fa_fwd_key_splits(B, H, Sq, Sk, D, causal, num_cus):
+    """Key-range parts fa_fwd gives the heaviest query tiles (1: no split)."""
+    return int(_capi.load().fa_fwd_key_splits(B, H, Sq, Sk, D, int(bool(causal)), num_cus))
 
 
 def fa_status_string(status):

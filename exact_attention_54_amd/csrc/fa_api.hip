@@ -8,7 +8,9 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <functional>
 #include <mutex>
+#include <vector>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -75,6 +77,153 @@ int hip_check(hipError_t e, const char* what) {
 int launched(const char* what) { return hip_check(hipGetLastError(), what); }
 
 int device_cu_count(int* out);
+int workspace_pool(hipMemPool_t* out);
+size_t ws_bytes(int64_t BH, int D, int ns);
+
+// Workspace of the key-split forward passes (partial O and LSE), one per
+// device, kept for the life of the process and grown when a call needs
+// more.  A call holds it from acquire to the end of its launches; every call
+// records an event on its stream after them, and a call on another stream
+// first makes its stream wait for that event, so calls on different streams
+// take turns on the GPU instead of racing.  Steady state: no allocation,
+// one event record per call.
+class FwdWorkspace {
+ public:
+  FwdWorkspace() = default;
+  FwdWorkspace(const FwdWorkspace&) = delete;
+  FwdWorkspace& operator=(const FwdWorkspace&) = delete;
+  ~FwdWorkspace();
+  // buffer of at least `bytes` bytes usable by work queued on `s` from now on
+  int acquire(size_t bytes, hipStream_t s, void** out);
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  int dev_ = -1;
+  hipStream_t stream_ = nullptr;
+};
+
+// Key-range split of a small prefill grid (fa::KeySplit): which query tiles
+// to split (ts .. nqt-1) and into how many parts, chosen by simulating the
+// dispatch.  Times are in units of one key tile of one query tile.
+struct SplitPlan {
+  int ts = 0, ns = 1;
+  int64_t grid = 0;
+};
+
+// Finishing time when the work items, in the kernel's issue order, each go
+// to the workgroup slot that frees first (each item costs its key tiles plus
+// kItemUnits for its Q load, pipeline fill and epilogue), but no less than
+// the whole job at the per-slot rate of a fully loaded chip (kFullLoad
+// times the rate of the last, lone tiles: measured on the D = 256 kernel,
+// where this model fits seven split choices of the (1, 16, 2048, 2048)
+// causal prefill within 6%).
+constexpr double kItemUnits = 3.0;
+constexpr double kFullLoad = 1.5;
+
+double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots) {
+  std::vector<double> finish((size_t)slots, 0.0);  // min-heap of slot finishing times
+  double total = 0.0;
+  auto push = [&](double w) {
+    std::pop_heap(finish.begin(), finish.end(), std::greater<double>());
+    finish.back() += w;
+    std::push_heap(finish.begin(), finish.end(), std::greater<double>());
+    total += w;
+  };
+  int th = nqt - 1, tl = ts - 1;
+  for (;;) {
+    const int wh = th >= ts ? (fa::fwd_tile_units(th, BM, BN, Sq, Sk, causal) + ns - 1) / ns : -1;
+    const int wl = tl >= 0 ? fa::fwd_tile_units(tl, BM, BN, Sq, Sk, causal) : -1;
+    if (wh < 0 && wl < 0) break;
+    if (wh >= wl) {
+      for (int i = 0; i < ns * BH; ++i) push(wh + kItemUnits);
+      --th;
+    } else {
+      for (int i = 0; i < BH; ++i) push(wl + kItemUnits);
+      --tl;
+    }
+  }
+  const double makespan = *std::max_element(finish.begin(), finish.end());
+  return std::max(makespan, kFullLoad * total / slots);
+}
+
+// Split only grids of at most two workgroups per slot, and only when the
+// modelled time plus the merge (its HBM bytes at ~4.5 TB/s, and a launch)
+// beats the unsplit grid by 10%.  unit_us: the time of one unit on one CU.
+SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int slots,
+                         double unit_us) {
+  SplitPlan best;
+  if (slots < 1 || (int64_t)nqt * BH > 2 * (int64_t)slots) return best;
+  static std::mutex mu;
+  struct Entry {
+    int key[8];
+    SplitPlan plan;
+  };
+  static Entry cache[16];
+  static int next = 0;
+  const int key[8] = {nqt, BH, BM, BN, D, Sq, Sk, (causal ? 1 : 0) | (slots << 1)};
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (std::equal(key, key + 8, e.key)) return e.plan;
+  double best_cost = 0.9 * fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, slots);
+  const int starts[4] = {0, nqt / 4, nqt / 2, 3 * nqt / 4};
+  const int parts[5] = {2, 3, 4, 6, 8};
+  for (int ts : starts) {
+    if (ts >= nqt || (!causal && ts > 0)) continue;
+    for (int ns : parts) {
+      if (ns > fa::fwd_tile_units(ts, BM, BN, Sq, Sk, causal)) continue;
+      const int64_t grid = (int64_t)BH * ((int64_t)(nqt - ts) * ns + ts);
+      if (grid > kMaxGrid) continue;
+      const double rows = (double)BH * (nqt - ts) * BM;
+      // partials read back, O and LSE written
+      const double bytes = rows * (ns * (D + 1) * 4.0 + D * 2.0 + 4.0);
+      const double merge_us = bytes / 4.5e6 + 2.0;
+      const double cost = fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, ts, ns, slots) + merge_us / unit_us;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best.ts = ts;
+        best.ns = ns;
+        best.grid = grid;
+      }
+    }
+  }
+  Entry& e = cache[next];
+  next = (next + 1) % 16;
+  std::copy(key, key + 8, e.key);
+  e.plan = best;
+  return best;
+}
+
+template <int D, int BN, int NW, bool CAUSAL>
+int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+                     float scale, hipStream_t stream, const SplitPlan& pl) {
+  using Cfg = fa::FwdCfg<D, BN, NW>;
+  const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
+  const int nsplit = nqt - pl.ts;
+  const int64_t rows = (int64_t)BH * nsplit * Cfg::BM;
+  if (rows > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  FwdWorkspace wsp;
+  void* ws = nullptr;
+  int rc = wsp.acquire(ws_bytes(rows, D, pl.ns), stream, &ws);
+  if (rc != FA_OK) return rc;
+  fa::KeySplit ksp;
+  ksp.ts = pl.ts;
+  ksp.ns = pl.ns;
+  ksp.ws_o = static_cast<float*>(ws);
+  ksp.ws_lse = ksp.ws_o + (size_t)rows * pl.ns * D;
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, false, true>), dim3((unsigned)pl.grid),
+                     dim3(Cfg::THREADS), 0, stream, static_cast<const _Float16*>(q),
+                     static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o),
+                     lse, Sq, Sk, BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
+  rc = launched("fa_fwd key-split kernel launch");
+  if (rc == FA_OK) {
+    constexpr int R = fa::MergeCfg<D>::ROWS;
+    hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
+                       ksp.ws_o, ksp.ws_lse, static_cast<_Float16*>(o), lse, Sq, Cfg::BM, pl.ts, nsplit, pl.ns,
+                       (int)rows);
+    rc = launched("fa_fwd key-split merge launch");
+  }
+  return rc;
+}
 
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
@@ -83,6 +232,16 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   const float c2 = scale * fa::kLog2e;
+  if constexpr (D == 256) {
+    // one workgroup per CU: a small causal grid is set by its heaviest tile
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != FA_OK) return rc;
+    const double unit_us = 4.0 * Cfg::BM * BN * D / 3.2e6;  // ~3.2 TFLOP/s per CU
+    const SplitPlan pl = plan_fwd_split(nqt, BH, Cfg::BM, BN, D, Sq, Sk, CAUSAL, cus * fa::fwd_wg_per_cu<D, NW>(),
+                                        unit_us);
+    if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl);
+  }
   hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
                      static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                      static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt, c2);
@@ -295,6 +454,62 @@ int workspace_pool(hipMemPool_t* out) {
   return FA_OK;
 }
 
+struct FwdWsSlot {
+  std::mutex mu;
+  void* buf = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;  // recorded after the last call's launches
+  hipStream_t stream = nullptr;
+  bool used = false;
+};
+FwdWsSlot g_fwd_ws[kMaxDevices];
+
+int FwdWorkspace::acquire(size_t bytes, hipStream_t s, void** out) {
+  int dev = 0;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != FA_OK) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+  FwdWsSlot& w = g_fwd_ws[dev];
+  lock_ = std::unique_lock<std::mutex>(w.mu);
+  if (!w.done) {
+    rc = hip_check(hipEventCreateWithFlags(&w.done, hipEventDisableTiming), "workspace event");
+    if (rc != FA_OK) return rc;
+  }
+  if (w.bytes < bytes) {
+    // growth (rare): wait until the last call's kernels are done with the old buffer
+    if (w.used) {
+      rc = hip_check(hipEventSynchronize(w.done), "workspace event wait");
+      if (rc != FA_OK) return rc;
+    }
+    if (w.buf) (void)hipFree(w.buf);
+    w.buf = nullptr;
+    w.bytes = 0;
+    rc = hip_check(hipMalloc(&w.buf, bytes), "workspace allocation");
+    if (rc != FA_OK) return rc;
+    w.bytes = bytes;
+  } else if (w.used && w.stream != s) {
+    rc = hip_check(hipStreamWaitEvent(s, w.done, 0), "workspace stream wait");
+    if (rc != FA_OK) return rc;
+  }
+  dev_ = dev;
+  stream_ = s;
+  *out = w.buf;
+  return FA_OK;
+}
+
+FwdWorkspace::~FwdWorkspace() {
+  if (dev_ < 0) return;
+  FwdWsSlot& w = g_fwd_ws[dev_];
+  if (hipEventRecord(w.done, stream_) == hipSuccess) {
+    w.used = true;
+    w.stream = stream_;
+  } else {
+    // no event to order the next call after this one: wait here instead
+    (void)hipStreamSynchronize(stream_);
+    w.used = false;
+  }
+}
+
 size_t ws_bytes(int64_t BH, int D, int ns) {
   const size_t floats = (size_t)BH * ns * (D + 1);
   return (floats * 4 + 255) / 256 * 256;
@@ -322,23 +537,18 @@ int run_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* 
   int rc = device_cu_count(&cus);
   if (rc != FA_OK) return rc;
   const int ns = splitd_parts((int64_t)nqt * BH, (Sk + 31) / 32, cus);
-  void* ws = nullptr;
   float* ws_o = nullptr;
   float* ws_lse = nullptr;
+  FwdWorkspace wsp;
   if (ns > 1) {
-    hipMemPool_t pool = nullptr;
-    rc = workspace_pool(&pool);
-    if (rc != FA_OK) return rc;
-    rc = hip_check(hipMallocFromPoolAsync(&ws, ws_bytes((int64_t)BH * Sq, D, ns), pool, s), "workspace allocation");
+    void* ws = nullptr;
+    rc = wsp.acquire(ws_bytes((int64_t)BH * Sq, D, ns), s, &ws);
     if (rc != FA_OK) return rc;
     ws_o = static_cast<float*>(ws);
     ws_lse = ws_o + (size_t)BH * Sq * ns * D;
   }
-  rc = causal ? launch_fwd_splitd<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse)
-              : launch_fwd_splitd<D, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse);
-  if (!ws) return rc;
-  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
-  return rc != FA_OK ? rc : frc;
+  return causal ? launch_fwd_splitd<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse)
+                : launch_fwd_splitd<D, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse);
 }
 
 int validate_decode(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
@@ -507,6 +717,31 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
                 : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
+}
+
+int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || num_cus < 1 || (causal != 0 && causal != 1)) return 0;
+  if ((int64_t)B * H > kMaxGrid) return 0;
+  const int BH = B * H;
+  switch (D) {
+    case 64:
+    case 128:
+      return 1;
+    case 256: {
+      using Cfg = fa::FwdCfg<256, 32, 4>;
+      const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
+      const double unit_us = 4.0 * Cfg::BM * 32 * 256 / 3.2e6;
+      return plan_fwd_split(nqt, BH, Cfg::BM, 32, 256, Sq, Sk, causal != 0, num_cus * fa::fwd_wg_per_cu<256, 4>(),
+                            unit_us).ns;
+    }
+    case 512:
+    case 1024: {
+      const int64_t nqt = (Sq + 31) / 32;
+      return splitd_parts(nqt * BH, (Sk + 31) / 32, num_cus);
+    }
+    default:
+      return 0;
+  }
 }
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {

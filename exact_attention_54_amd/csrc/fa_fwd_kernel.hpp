@@ -86,11 +86,36 @@ struct VarlenArgs {
   int H, total_q, total_k, max_q, max_k;
 };
 
-template <int D, int BN, int NW, bool CAUSAL, bool VARLEN = false>
+// Key-range split of the heavier query tiles, for grids too small to keep
+// every CU busy until the end: query tiles ts .. nqt-1 are each processed as
+// ns workgroups over consecutive parts of their key range (the split-KV idea
+// of the decode, "Adaptive High-Performance Attention Kernels in CUDA",
+// Split-K / Flash-Decoding, applied to the tiles whose causal key range is
+// longest).  Each part writes its normalised fp32 partial O and its log-sum-
+// exp to rows of [rows, ns, D] / [rows, ns] (row = (slice, tile - ts, row in
+// tile)); fwd_merge_kernel combines them.  Tiles below ts run whole and write
+// O and LSE directly.  Work items are issued heaviest first: the split parts
+// and the whole tiles are two lists of falling weight, merged by weight.
+struct KeySplit {
+  int ts;        // first split query tile
+  int ns;        // parts per split tile
+  float* ws_o;   // [BH * (nqt - ts) * BM, ns, D]
+  float* ws_lse; // [BH * (nqt - ts) * BM, ns]
+};
+
+// Key tiles of BN keys that query tile t (BM rows) visits.
+__host__ __device__ inline int fwd_tile_units(int t, int BM, int BN, int Sq, int Sk, bool causal) {
+  const int all = (Sk + BN - 1) / BN;
+  if (!causal) return all;
+  const int hi = min(min((t + 1) * BM, Sq), Sk);
+  return min(all, (hi + BN - 1) / BN);
+}
+
+template <int D, int BN, int NW, bool CAUSAL, bool VARLEN = false, bool KSPLIT = false>
 __global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<D, NW>()))
 fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
            const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
-           int Sq, int Sk, int BH, int nqt, float c2, VarlenArgs va = {}) {
+           int Sq, int Sk, int BH, int nqt, float c2, VarlenArgs va = {}, KeySplit ksp = {}) {
   using C = FwdCfg<D, BN, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
@@ -109,9 +134,40 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // bh = 8 g + x, so all query tiles of a slice run back to back on one XCD
   // (ids are dealt to the 8 XCDs round robin) and share its L2 copy of the
   // slice's K / V, whatever the number of slices.
-  const int rank = VARLEN ? (int)((blockIdx.x >> 3) % (unsigned)nqt) : (int)(blockIdx.x / BH);
-  const int bh = VARLEN ? (int)((blockIdx.x >> 3) / (unsigned)nqt) * 8 + (int)(blockIdx.x & 7)
-                        : (int)(blockIdx.x - rank * BH);
+  int rank = VARLEN ? (int)((blockIdx.x >> 3) % (unsigned)nqt) : (int)(blockIdx.x / BH);
+  int bh = VARLEN ? (int)((blockIdx.x >> 3) / (unsigned)nqt) * 8 + (int)(blockIdx.x & 7)
+                  : (int)(blockIdx.x - rank * BH);
+  // Split grids: walk the two weight-ordered lists (parts of tiles ts..nqt-1,
+  // whole tiles 0..ts-1, each from the top) to this workgroup's item.  Within
+  // a tile the items are part-major, slice-minor, so a slice keeps its XCD.
+  int part = 0, nparts = 1;
+  if constexpr (KSPLIT) {
+    int idx = (int)blockIdx.x, th = nqt - 1, tl = ksp.ts - 1;
+    for (;;) {
+      const int wh = th >= ksp.ts ? (fwd_tile_units(th, C::BM, BN, Sq, Sk, CAUSAL) + ksp.ns - 1) / ksp.ns : -1;
+      const int wl = tl >= 0 ? fwd_tile_units(tl, C::BM, BN, Sq, Sk, CAUSAL) : -1;
+      if (wh < 0 && wl < 0) return;  // past the last item
+      if (wh >= wl) {
+        if (idx < ksp.ns * BH) {
+          part = idx / BH;
+          bh = idx - part * BH;
+          nparts = ksp.ns;
+          rank = CAUSAL ? nqt - 1 - th : th;
+          break;
+        }
+        idx -= ksp.ns * BH;
+        --th;
+      } else {
+        if (idx < BH) {
+          bh = idx;
+          rank = CAUSAL ? nqt - 1 - tl : tl;
+          break;
+        }
+        idx -= BH;
+        --tl;
+      }
+    }
+  }
   if (VARLEN && bh >= BH) return;  // the grid rounds the slice count up to a multiple of 8
   // Slice of this work item: base pointers, lengths and the row stride (in
   // elements) of q, k, v, o.  Dense [B, H, S, D]: rows D apart.  Packed
@@ -162,8 +218,15 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
 
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + C::BM, Sk) + BN - 1) / BN) : nkt_all;
-  // last key tile this wavefront needs (-1: none, its rows are all past Sq)
-  const int jlast = (qw >= Sq) ? -1 : (CAUSAL ? min(nkt - 1, (qw + 31) / BN) : nkt - 1);
+  // key tiles [kb, ke) of this work item (a part of the range when split)
+  int kb = 0, ke = nkt;
+  if (KSPLIT && nparts > 1) {
+    const int c = (nkt + nparts - 1) / nparts;
+    kb = min(part * c, nkt);
+    ke = min(kb + c, nkt);
+  }
+  // last key tile this wavefront needs (below kb: none, e.g. rows past Sq)
+  const int jlast = (qw >= Sq) ? -1 : (CAUSAL ? min(ke - 1, (qw + 31) / BN) : ke - 1);
 
   // Global byte offsets (inside one tile) of the 16-byte chunks this lane
   // moves into LDS: wavefront w fills 1 KiB blocks w*LPW .. w*LPW+LPW-1 of
@@ -332,22 +395,24 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   };
   auto tile_needs_mask = [&](int kt) { return (kt * BN + BN > Sk) || (CAUSAL && kt * BN + BN - 1 > qw); };
 
-  // Prologue: K(0), V(0), K(1) resident, S(0) computed, masked and maxed.
-  load_k(0, 0);
-  load_v(0, 0);
-  if (nkt > 1) load_k(1, 1);
+  // Prologue: K(kb), V(kb), K(kb+1) resident, S(kb) computed, masked and maxed.
+  if (!KSPLIT || kb < ke) {
+    load_k(kb, kb & 1);
+    load_v(kb, kb & 1);
+  }
+  if (kb + 1 < ke) load_k(kb + 1, (kb + 1) & 1);
   wait_vmem_all();
   __syncthreads();
-  if (jlast >= 0) {
-    qk(0, s_cur);
-    if (tile_needs_mask(0)) mask_and_max(s_cur, 0, std::true_type{});
-    else mask_and_max(s_cur, 0, std::false_type{});
+  if (jlast >= kb) {
+    qk(kb & 1, s_cur);
+    if (tile_needs_mask(kb)) mask_and_max(s_cur, kb, std::true_type{});
+    else mask_and_max(s_cur, kb, std::false_type{});
   }
   __syncthreads();  // K stage 0 is refilled with K(2) below
 
   auto begin_tile = [&](int kt) {
-    if (kt + 2 < nkt) load_k(kt + 2, kt & 1);
-    if (kt + 1 < nkt) load_v(kt + 1, (kt + 1) & 1);
+    if (kt + 2 < ke) load_k(kt + 2, kt & 1);
+    if (kt + 1 < ke) load_v(kt + 1, (kt + 1) & 1);
   };
   auto rescale_if_grown = [&]() {
     if (wave_any(grow)) {  // rare: some row max grew by more than 2^8
@@ -372,7 +437,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   const int kmask = min(CAUSAL ? (qw + 1) / BN : nkt_all, (Sk % BN) ? nkt_all - 1 : nkt_all);
   const int kclean = min(kmask - 1, jlast);
   f32x16 s_alt[C::NKB];
-  int kt = 0;
+  int kt = kb;
   for (; kt + 2 <= kclean; kt += 2) {
     begin_tile(kt);
     rescale_if_grown();
@@ -384,13 +449,13 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     end_tile();
   }
   // The last few tiles (diagonal, ragged tail, past this wavefront's rows).
-  for (; kt < nkt; ++kt) {
+  for (; kt < ke; ++kt) {
     begin_tile(kt);
     if (kt <= jlast) {
       rescale_if_grown();
       // the mask of S(kt+1) is a compile-time variant, so unmasked tiles
       // carry no compare/select work
-      if (kt + 1 < nkt) {
+      if (kt + 1 < ke) {
         if (tile_needs_mask(kt + 1)) step(kt, std::true_type{}, std::true_type{});
         else step(kt, std::false_type{}, std::true_type{});
       } else {
@@ -406,6 +471,26 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   // a row with no key at all (an empty key range of a packed sequence):
   // O = 0, LSE = -inf
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (KSPLIT && nparts > 1) {
+    // one part of a split tile: normalised fp32 partial O and its log-sum-
+    // exp, in the merge kernel's [row, part, D] / [row, part] order
+    if (qi < Sq) {
+      const size_t row = ((size_t)bh * (nqt - ksp.ts) + (qt - ksp.ts)) * C::BM + (qi - q0);
+      float* po = ksp.ws_o + (row * nparts + part) * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = oacc[db][4 * jg + e] * inv;
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * jg + 4 * hh) = val;
+        }
+      if (hh == 0)
+        ksp.ws_lse[row * nparts + part] = (l_tot > 0.f) ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   char* Os = smem + w * (32 * D * 2);
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
@@ -430,6 +515,59 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     }
   }
   if (hh == 0 && qi < Sq) ls[qi] = (l_tot > 0.f) ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+}
+
+// Merge of a key-split prefill: for each row of the split query tiles,
+// lse = ln sum_p e^(lse_p) and O = sum_p e^(lse_p - lse) O_p, the log-sum-exp
+// combination of partial softmax results ("Adaptive High-Performance
+// Attention Kernels in CUDA", Split-K / Flash-Decoding, phase two).  D/4
+// threads per row, 4 consecutive d each (16-byte loads); 256 / (D/4) rows
+// per workgroup.  Row = (slice, tile - ts, row in tile), written to
+// O[slice, (ts + tile) * BM + row] and LSE at the same position.
+template <int D>
+struct MergeCfg {
+  static constexpr int TPR = D / 4;         // threads per row
+  static constexpr int ROWS = 256 / TPR;    // rows per workgroup
+  static_assert(D % 4 == 0 && TPR <= 256 && 256 % TPR == 0, "merge geometry");
+};
+
+template <int D>
+__global__ void __launch_bounds__(256)
+fwd_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, _Float16* __restrict__ O,
+                 float* __restrict__ LSE, int Sq, int BM, int ts, int nsplit, int ns, int rows) {
+  using M = MergeCfg<D>;
+  const int row = (int)blockIdx.x * M::ROWS + (int)threadIdx.x / M::TPR;
+  const int d0 = 4 * ((int)threadIdx.x % M::TPR);
+  if (row >= rows) return;
+  const int r = row % BM;
+  const int tl = (row / BM) % nsplit;
+  const int bh = row / (BM * nsplit);
+  const int q = (ts + tl) * BM + r;
+  if (q >= Sq) return;
+  const float* lp = ws_lse + (size_t)row * ns;
+  const float* op = ws_o + (size_t)row * ns * D + d0;
+  const size_t out = (size_t)bh * Sq + q;
+  float mx = kNegInf;
+  for (int p = 0; p < ns; ++p) mx = fmaxf(mx, lp[p]);
+  h4 res;
+  if (mx == kNegInf) {  // no key in any part: O = 0, LSE = -inf
+    res = h4{0, 0, 0, 0};
+  } else {
+    float den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < ns; ++p) {
+      const float wgt = exp2_fast((lp[p] - mx) * kLog2e);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(op + (size_t)p * D);
+      den += wgt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += wgt * x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = (_Float16)(num[e] / den);
+    mx += __builtin_logf(den);
+  }
+  *reinterpret_cast<h4*>(O + out * D + d0) = res;
+  if (d0 == 0) LSE[out] = mx;
 }
 
 }  // namespace fa

@@ -46,8 +46,9 @@
  *             allocation; fa_last_error() then names it.
  *   Threads   calls hold no global mutable state apart from a per-device CU
  *             count cache, a per-device workspace memory pool (created under
- *             a lock) and a thread-local error message; they may be made
- *             from several threads at once.
+ *             a lock), a per-device forward workspace (used under a lock, see
+ *             fa_fwd), a small cache of fa_fwd split plans and a thread-local
+ *             error message; they may be made from several threads at once.
  */
 #ifndef FA_H
 #define FA_H
@@ -83,8 +84,16 @@ enum fa_status {
  * slice of D, and their partial scores are summed through LDS.  When those
  * (query tile, slice) work items are fewer than the CUs, the Split-D key
  * range is also split and the parts merged with log-sum-exp weights
- * ("Split-KV" of the same list); their fp32 partials then live in a
- * workspace from the library's stream-ordered pool (see fa_decode_splitkv).
+ * ("Split-KV" of the same list).  At D = 256, where one workgroup fills a
+ * CU, a grid of at most two workgroups per CU whose heaviest (causal)
+ * query tiles would leave most CUs idle near the end also has the key
+ * ranges of those tiles split, when fa_fwd_key_splits() says it pays; a
+ * second kernel merges the parts.  Split calls keep their fp32 partials in
+ * a per-device workspace that the library allocates on first need, grows
+ * when a call needs more (after the previous call's kernels are done with
+ * it) and keeps until the process ends; a call on another stream than the
+ * previous split call first waits on the GPU for that call's kernels, so
+ * split calls on one device run one after another.
  * Any Sq works, including Sq = 1.  o and lse must not overlap the inputs.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -230,6 +239,19 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * Sk).  Pure host arithmetic; returns 0 for invalid sizes.
  */
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
+
+/*
+ * fa_fwd_key_splits -- the number of key-range parts that fa_fwd gives the
+ * heaviest query tiles of these sizes on a device with num_cus CUs (1: no
+ * split), the same choice fa_fwd makes ("Adaptive High-Performance
+ * Attention Kernels in CUDA", Split-K / Flash-Decoding, applied to prefill
+ * query tiles).  D = 256: chosen by simulating the dispatch of the
+ * work items (heaviest first, each to the CU that frees first) against the
+ * cost of merging the parts.  D = 512, 1024: the Split-D key split (enough
+ * parts to give every CU a work item when there are fewer than CUs, at most
+ * 16).  D = 64, 128: 1.  Pure host arithmetic; returns 0 for invalid sizes.
+ */
+int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
 
 /* fa_status_string -- static text for an FA_* status code. */
 const char* fa_status_string(int status);

@@ -145,6 +145,37 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
     assert lib.fa_decode_auto_splits(B, H, Sk, cus) == want
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk,D,causal,cus,want", [
+    (1, 32, 4096, 4096, 128, 1, 256, 1),   # D <= 128: never split
+    (1, 1, 4096, 4096, 64, 1, 256, 1),
+    (1, 16, 2048, 2048, 256, 1, 256, 1),   # 256 tiles, one per CU: the merge would cost about what it saves
+    (1, 16, 2048, 2048, 256, 0, 256, 1),   # full key range everywhere: every CU equally loaded
+    (1, 16, 1024, 1024, 256, 1, 256, 2),   # 128 tiles on 256 CUs
+    (1, 8, 4096, 4096, 256, 1, 256, 2),    # heaviest tiles twice the mean
+    (1, 4, 2048, 2048, 256, 0, 256, 3),    # 64 tiles on 256 CUs
+    (1, 2, 1000, 1000, 256, 1, 256, 4),
+    (8, 32, 2048, 2048, 256, 1, 256, 1),   # 4096 tiles: more than two per CU, never split
+    (1, 4, 512, 512, 1024, 0, 256, 4),     # Split-D: 64 work items -> 4 parts
+    (1, 8, 1024, 1024, 512, 0, 256, 1),    # Split-D: 256 work items fill the CUs
+    (0, 1, 16, 16, 256, 0, 256, 0),        # invalid sizes
+    (1, 1, 16, 16, 96, 0, 256, 0),
+    (1, 1, 16, 16, 256, 2, 256, 0),
+    (1, 1, 16, 16, 256, 0, 0, 0),
+])
+def test_fwd_key_splits(lib, B, H, Sq, Sk, D, causal, cus, want):
+    assert lib.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus) == want
+
+
+def test_fwd_key_splits_stays_within_sensible_bounds(lib):
+    # any valid size: at most 8 parts at D = 256, none when the grid already
+    # holds more than two workgroups per CU
+    for B, H, S, causal in [(1, 1, 1, 0), (1, 1, 129, 1), (1, 3, 777, 1), (2, 5, 3000, 0), (1, 64, 1024, 1)]:
+        ns = lib.fa_fwd_key_splits(B, H, S, S, 256, causal, 256)
+        assert 1 <= ns <= 8
+        if B * H * -(-S // 128) > 512:
+            assert ns == 1
+
+
 def test_status_strings(lib):
     assert _capi.status_name(0) == "ok"
     assert _capi.status_name(1) == "invalid argument"

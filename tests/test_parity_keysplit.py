@@ -1,0 +1,139 @@
+"""GPU parity of the key-split D = 256 prefill against the CPU fp64 oracle.
+
+fa_fwd splits the key range of the heaviest query tiles of a small D = 256
+grid into parts and merges them with log-sum-exp weights (the split-KV
+scheme of "Adaptive High-Performance Attention Kernels in CUDA", Split-K /
+Flash-Decoding, on prefill tiles).  Every shape here is checked to be one
+that fa_fwd_key_splits() splits on this device, so these tests run the
+split kernel and its merge; the bar is the one of every prefill: max |dO|
+<= 2e-3, max |dLSE| <= 1e-3.  Also covered: bitwise repeatability, the
+workspace growing between calls queued without a sync, and split calls on
+two streams taking turns on the shared workspace.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+LSE_TOL = 1e-3
+D = 256
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import exact_attention_54_amd as fa
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU (the HIP library has no CPU path)"
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    return torch, dev, fa, cus
+
+
+def inputs(env, B, H, Sq, Sk, causal, seed):
+    torch, dev, fa, cus = env
+    ns = fa.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus)
+    assert ns > 1, f"{(B, H, Sq, Sk, causal)} is not split on {cus} CUs"
+    q, k, v = make_qkv(B, H, Sq, Sk, D, seed=seed)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    return (q, k, v), (qd, kd, vd), ns
+
+
+def check(o, lse, O, L, what):
+    o = o.float().cpu().numpy() if hasattr(o, "cpu") else o
+    lse = lse.cpu().numpy() if hasattr(lse, "cpu") else lse
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{what}: non-finite output"
+    eo = float(np.abs(o - O).max())
+    el = float(np.abs(lse - L).max())
+    print(f"{what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= O_TOL, f"{what}: max|dO| = {eo:.3e}"
+    assert el <= LSE_TOL, f"{what}: max|dLSE| = {el:.3e}"
+
+
+def test_workspace_grows_between_queued_calls(env):
+    # small split call, the largest split call of this file, small again,
+    # queued back to back: the second grows the workspace after the first's
+    # kernels are done with it
+    torch = env[0]
+    small = inputs(env, 1, 2, 1000, 1000, True, seed=31)
+    large = inputs(env, 1, 4, 2048, 2048, False, seed=32)
+    seq = [(small, True), (large, False), (small, True)]
+    outs = [env[2].fa_fwd(*case[1], causal=causal, scale=1 / 16) for case, causal in seq]
+    torch.cuda.synchronize()
+    for ((host, _, ns), causal), (o, lse) in zip(seq, outs):
+        O, L = oracle.attention(*host, causal, 1 / 16)
+        check(o, lse, O, L, f"queued {host[0].shape} causal={causal} ns={ns}")
+
+
+SPLIT = [
+    # B, H, Sq, Sk, causal
+    (1, 16, 1024, 1024, True),
+    (1, 4, 2048, 2048, False),
+    (1, 2, 1000, 1000, True),
+    (1, 3, 200, 333, False),
+    (1, 1, 777, 1500, True),
+    (1, 2, 300, 100, True),     # more queries than keys
+    (2, 1, 129, 1000, False),   # a ragged query tile of one row
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT, ids=["x".join(map(str, s)) for s in SPLIT])
+def test_split_prefill_matches_oracle(env, shape):
+    B, H, Sq, Sk, causal = shape
+    host, dev_in, ns = inputs(env, B, H, Sq, Sk, causal, seed=100 + Sq + Sk)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = env[2].fa_fwd(*dev_in, causal=causal, scale=scale)
+    env[0].cuda.synchronize()
+    O, L = oracle.attention(*host, causal, scale)
+    check(o, lse, O, L, f"split {shape} ns={ns}")
+
+
+def test_split_long_causal_sampled_rows(env):
+    # (1, 8, 4096, 4096): the split tiles are the last quarter; rows sampled
+    # across every tile, both ends of each split tile among them
+    torch = env[0]
+    host, dev_in, ns = inputs(env, 1, 8, 4096, 4096, True, seed=41)
+    o, lse = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = [(0, h, i) for h in (0, 7) for i in (0, 127, 128, 3071, 3072, 3199, 3200, 4095)]
+    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, 8, 48), rng.integers(0, 4096, 48))]
+    O, L = oracle.attention_rows(*host, True, 1 / 16, rows)
+    idx = tuple(np.array(rows).T)
+    check(o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], O, L, f"long causal sampled rows ns={ns}")
+
+
+def test_split_run_to_run_bitwise(env):
+    torch = env[0]
+    _, dev_in, _ = inputs(env, 1, 16, 1024, 1024, True, seed=51)
+    a = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
+    b = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_split_calls_on_two_streams(env):
+    # split calls alternate between two streams with no host sync: each
+    # waits on the GPU for the previous call's use of the shared workspace
+    torch, dev, fa, _ = env
+    shapes = [(1, 2, 1000, 1000, True), (1, 3, 200, 333, False)]
+    cases = [inputs(env, B, H, Sq, Sk, c, seed=60 + i) + (c,) for i, (B, H, Sq, Sk, c) in enumerate(shapes)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]  # default priority
+    outs = []
+    for rep in range(3):
+        for i, (host, dev_in, ns, causal) in enumerate(cases):
+            with torch.cuda.stream(streams[i]):
+                outs.append((i, fa.fa_fwd(*dev_in, causal=causal, scale=1 / 16)))
+    for s in streams:
+        s.synchronize()
+    refs = [oracle.attention(*host, causal, 1 / 16) for host, _, _, causal in cases]
+    for n, (i, (o, lse)) in enumerate(outs):
+        check(o, lse, *refs[i], f"stream {i} call {n}")
