@@ -413,6 +413,26 @@ def main():
     t_d256 = time_launches(torch, d256, args.steps)
     tflops_d256 = prefill_flops(w5.B, w5.H, w5.Sq, w5.Sk, w5.D, True) / t_d256 / 1e12
     log(f"D=256 causal prefill (1,16,2048,2048,256): {t_d256 * 1e6:.1f} us = {tflops_d256:.1f} TFLOPS")
+
+    # One GPU's share of the LLaMA-7B-shaped prefill sharded by heads over 8
+    # GPUs: 4 of the 32 heads, (1, 4, 4096, 4096, 128) causal.  128 query
+    # tiles leave most CUs idle, so fa_fwd splits the key ranges of the
+    # heaviest ones (fa_fwd_key_splits parts) and merges them.
+    hs = 4
+    qs_, ks_, vs_ = (x[:, :hs].contiguous() for x in (q3, k3, v3))
+    os_ = torch.empty_like(qs_)
+    ls_ = torch.empty((1, hs, w3.Sq), dtype=torch.float32, device=dev)
+
+    def shard():
+        fa.fa_fwd(qs_, ks_, vs_, os_, ls_, causal=True, scale=w3.scale)
+
+    for _ in range(args.warmup):
+        shard()
+    t_shard = time_launches(torch, shard, args.steps)
+    tflops_shard = prefill_flops(1, hs, w3.Sq, w3.Sk, w3.D, True) / t_shard / 1e12
+    shard_parts = fa.fa_fwd_key_splits(1, hs, w3.Sq, w3.Sk, w3.D, True, cus)
+    log(f"head-shard prefill (1,{hs},4096,4096,128): {t_shard * 1e6:.1f} us = {tflops_shard:.1f} TFLOPS "
+        f"({shard_parts} key parts)")
     del q5, k5, v5, o5, l5
     # the small (8,16,256,256,64) shape, both masks: launch-sized work
     w2 = WORKLOADS["small"]
@@ -521,6 +541,10 @@ def main():
             "d256_prefill_tflops": round(tflops_d256, 3),
             "d256_prefill_frac_of_peak": round(tflops_d256 / PEAK_FP16_TFLOPS, 4),
             "d256_prefill_us": round(t_d256 * 1e6, 2),
+            "head_shard_prefill_tflops": round(tflops_shard, 3),
+            "head_shard_prefill_frac_of_peak": round(tflops_shard / PEAK_FP16_TFLOPS, 4),
+            "head_shard_prefill_us": round(t_shard * 1e6, 2),
+            "head_shard_key_parts": shard_parts,
             **small,
             **context,
             **{"splitd_" + k: x for k, x in splitd.items()},

@@ -110,20 +110,35 @@ struct SplitPlan {
   int64_t grid = 0;
 };
 
-// Finishing time when the work items, in the kernel's issue order, each go
-// to the workgroup slot that frees first (each item costs its key tiles plus
-// kItemUnits for its Q load, pipeline fill and epilogue), but no less than
-// the whole job at the per-slot rate of a fully loaded chip (kFullLoad
-// times the rate of the last, lone tiles: measured on the D = 256 kernel,
-// where this model fits seven split choices of the (1, 16, 2048, 2048)
-// causal prefill within 6%).
-constexpr double kItemUnits = 3.0;
-constexpr double kFullLoad = 1.5;
+// Cost model of a split plan, per kernel, fitted to timed plans (kernels
+// and merge, rocprofv3 kernel trace):
+//   D = 256, one workgroup per CU: seven plans of the (1, 16, 2048, 2048)
+//     causal shape, all within 6%;
+//   D <= 128, the 4-wavefront kernel: 34 plans over five shapes, within 26%,
+//     with every split decision right.
+// A work item costs its key tiles at unit_us each plus item_us of fixed
+// work (Q load, pipeline fill, epilogue); items go, heaviest first, to the
+// CU that frees first; and the whole job takes at least full_load times its
+// mean time per CU (the clock of a fully loaded chip is lower than that of
+// one whose last heavy tiles run alone).
+struct SplitModel {
+  double unit_us, item_us, full_load, min_gain;
+  bool causal_only;
+};
 
-double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots) {
+SplitModel fwd_split_model(int D) {
+  if (D == 256) return {4.0 * 128 * 32 * 256 / 3.2e6, 3.9, 1.5, 0.9, false};
+  // a lone 4-wavefront workgroup of 128 rows runs a 64-key tile of D = 128
+  // in ~1.1 us; non-causal grids measured no gain from splitting
+  return {1.1 * D / 128.0, 6.6, 1.0, 0.8, true};
+}
+
+double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots,
+                      const SplitModel& m) {
   std::vector<double> finish((size_t)slots, 0.0);  // min-heap of slot finishing times
   double total = 0.0;
-  auto push = [&](double w) {
+  auto push = [&](int units) {
+    const double w = units * m.unit_us + m.item_us;
     std::pop_heap(finish.begin(), finish.end(), std::greater<double>());
     finish.back() += w;
     std::push_heap(finish.begin(), finish.end(), std::greater<double>());
@@ -135,24 +150,24 @@ double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool caus
     const int wl = tl >= 0 ? fa::fwd_tile_units(tl, BM, BN, Sq, Sk, causal) : -1;
     if (wh < 0 && wl < 0) break;
     if (wh >= wl) {
-      for (int i = 0; i < ns * BH; ++i) push(wh + kItemUnits);
+      for (int i = 0; i < ns * BH; ++i) push(wh);
       --th;
     } else {
-      for (int i = 0; i < BH; ++i) push(wl + kItemUnits);
+      for (int i = 0; i < BH; ++i) push(wl);
       --tl;
     }
   }
   const double makespan = *std::max_element(finish.begin(), finish.end());
-  return std::max(makespan, kFullLoad * total / slots);
+  return std::max(makespan, m.full_load * total / slots);
 }
 
-// Split only grids of at most two workgroups per slot, and only when the
+// Split only grids of at most two work items per CU, and only when the
 // modelled time plus the merge (its HBM bytes at ~4.5 TB/s, and a launch)
-// beats the unsplit grid by 10%.  unit_us: the time of one unit on one CU.
-SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int slots,
-                         double unit_us) {
+// beats the unsplit grid by the model's margin.
+SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus) {
   SplitPlan best;
-  if (slots < 1 || (int64_t)nqt * BH > 2 * (int64_t)slots) return best;
+  const SplitModel m = fwd_split_model(D);
+  if (cus < 1 || (int64_t)nqt * BH > 2 * (int64_t)cus || (m.causal_only && !causal)) return best;
   static std::mutex mu;
   struct Entry {
     int key[8];
@@ -160,11 +175,11 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
   };
   static Entry cache[16];
   static int next = 0;
-  const int key[8] = {nqt, BH, BM, BN, D, Sq, Sk, (causal ? 1 : 0) | (slots << 1)};
+  const int key[8] = {nqt, BH, BM, BN, D, Sq, Sk, (causal ? 1 : 0) | (cus << 1)};
   std::lock_guard<std::mutex> lock(mu);
   for (const Entry& e : cache)
     if (std::equal(key, key + 8, e.key)) return e.plan;
-  double best_cost = 0.9 * fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, slots);
+  double best_cost = m.min_gain * fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, cus, m);
   const int starts[4] = {0, nqt / 4, nqt / 2, 3 * nqt / 4};
   const int parts[5] = {2, 3, 4, 6, 8};
   for (int ts : starts) {
@@ -176,8 +191,7 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
       const double rows = (double)BH * (nqt - ts) * BM;
       // partials read back, O and LSE written
       const double bytes = rows * (ns * (D + 1) * 4.0 + D * 2.0 + 4.0);
-      const double merge_us = bytes / 4.5e6 + 2.0;
-      const double cost = fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, ts, ns, slots) + merge_us / unit_us;
+      const double cost = fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, ts, ns, cus, m) + bytes / 4.5e6 + 2.0;
       if (cost < best_cost) {
         best_cost = cost;
         best.ts = ts;
@@ -232,14 +246,12 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   const float c2 = scale * fa::kLog2e;
-  if constexpr (D == 256) {
-    // one workgroup per CU: a small causal grid is set by its heaviest tile
+  if constexpr (D == 256 || NW == 4) {
+    // small grids: the heaviest (causal) tiles, or too few tiles, leave CUs idle
     int cus = 0;
     int rc = device_cu_count(&cus);
     if (rc != FA_OK) return rc;
-    const double unit_us = 4.0 * Cfg::BM * BN * D / 3.2e6;  // ~3.2 TFLOP/s per CU
-    const SplitPlan pl = plan_fwd_split(nqt, BH, Cfg::BM, BN, D, Sq, Sk, CAUSAL, cus * fa::fwd_wg_per_cu<D, NW>(),
-                                        unit_us);
+    const SplitPlan pl = plan_fwd_split(nqt, BH, Cfg::BM, BN, D, Sq, Sk, CAUSAL, cus);
     if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl);
   }
   hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
@@ -725,14 +737,17 @@ int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_c
   const int BH = B * H;
   switch (D) {
     case 64:
-    case 128:
-      return 1;
+    case 128: {
+      // the 8-wavefront kernel (grids that give every CU a workgroup) is never split
+      if ((int64_t)BH * ((Sq + 255) / 256) >= num_cus) return 1;
+      using Cfg = fa::FwdCfg<128, 64, 4>;
+      const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
+      return plan_fwd_split(nqt, BH, Cfg::BM, 64, D, Sq, Sk, causal != 0, num_cus).ns;
+    }
     case 256: {
       using Cfg = fa::FwdCfg<256, 32, 4>;
       const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-      const double unit_us = 4.0 * Cfg::BM * 32 * 256 / 3.2e6;
-      return plan_fwd_split(nqt, BH, Cfg::BM, 32, 256, Sq, Sk, causal != 0, num_cus * fa::fwd_wg_per_cu<256, 4>(),
-                            unit_us).ns;
+      return plan_fwd_split(nqt, BH, Cfg::BM, 32, 256, Sq, Sk, causal != 0, num_cus).ns;
     }
     case 512:
     case 1024: {

@@ -146,8 +146,12 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
 
 
 @pytest.mark.parametrize("B,H,Sq,Sk,D,causal,cus,want", [
-    (1, 32, 4096, 4096, 128, 1, 256, 1),   # D <= 128: never split
-    (1, 1, 4096, 4096, 64, 1, 256, 1),
+    (1, 32, 4096, 4096, 128, 1, 256, 1),   # 8-wavefront grid (every CU has a workgroup): never split
+    (1, 4, 4096, 4096, 128, 1, 256, 3),    # one GPU's 4 heads of it: 128 tiles, heaviest 32x the lightest
+    (1, 2, 8192, 8192, 128, 1, 256, 4),
+    (1, 1, 4096, 4096, 64, 1, 256, 4),
+    (1, 8, 2048, 2048, 128, 0, 256, 1),    # D <= 128 non-causal: measured no gain, never split
+    (2, 8, 1024, 1024, 128, 1, 256, 1),    # short tiles: the merge costs what the balance saves
     (1, 16, 2048, 2048, 256, 1, 256, 1),   # 256 tiles, one per CU: the merge would cost about what it saves
     (1, 16, 2048, 2048, 256, 0, 256, 1),   # full key range everywhere: every CU equally loaded
     (1, 16, 1024, 1024, 256, 1, 256, 2),   # 128 tiles on 256 CUs

@@ -1,7 +1,7 @@
-"""GPU parity of the key-split D = 256 prefill against the CPU fp64 oracle.
+"""GPU parity of the key-split prefill against the CPU fp64 oracle.
 
-fa_fwd splits the key range of the heaviest query tiles of a small D = 256
-grid into parts and merges them with log-sum-exp weights (the split-KV
+fa_fwd splits the key range of the heaviest query tiles of a small grid
+(D = 256; causal D <= 128 grids of the 4-wavefront kernel) into parts and merges them with log-sum-exp weights (the split-KV
 scheme of "Adaptive High-Performance Attention Kernels in CUDA", Split-K /
 Flash-Decoding, on prefill tiles).  Every shape here is checked to be one
 that fa_fwd_key_splits() splits on this device, so these tests run the
@@ -37,10 +37,10 @@ def env():
     return torch, dev, fa, cus
 
 
-def inputs(env, B, H, Sq, Sk, causal, seed):
+def inputs(env, B, H, Sq, Sk, causal, seed, D=D):
     torch, dev, fa, cus = env
     ns = fa.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus)
-    assert ns > 1, f"{(B, H, Sq, Sk, causal)} is not split on {cus} CUs"
+    assert ns > 1, f"{(B, H, Sq, Sk, D, causal)} is not split on {cus} CUs"
     q, k, v = make_qkv(B, H, Sq, Sk, D, seed=seed)
     qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
     return (q, k, v), (qd, kd, vd), ns
@@ -137,3 +137,41 @@ def test_split_calls_on_two_streams(env):
     refs = [oracle.attention(*host, causal, 1 / 16) for host, _, _, causal in cases]
     for n, (i, (o, lse)) in enumerate(outs):
         check(o, lse, *refs[i], f"stream {i} call {n}")
+
+
+SPLIT_SMALL_D = [
+    # B, H, Sq, Sk, D (causal)
+    (1, 2, 1000, 1000, 128),
+    (1, 1, 1000, 3000, 128),    # more keys than queries
+    (1, 1, 3000, 1000, 128),    # more queries than keys
+    (1, 2, 1000, 1000, 64),
+    (1, 2, 2000, 2000, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SMALL_D, ids=["x".join(map(str, s)) for s in SPLIT_SMALL_D])
+def test_split_small_head_dims_match_oracle(env, shape):
+    B, H, Sq, Sk, d = shape
+    host, dev_in, ns = inputs(env, B, H, Sq, Sk, True, seed=200 + Sq + Sk + d, D=d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = env[2].fa_fwd(*dev_in, causal=True, scale=scale)
+    env[0].cuda.synchronize()
+    O, L = oracle.attention(*host, True, scale)
+    check(o, lse, O, L, f"split D={d} {shape} ns={ns}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_head_shard_of_llama_prefill_sampled_rows(env, d):
+    # (1, 4, 4096, 4096): one GPU's 4 of the 32 heads when the LLaMA-7B-shaped
+    # prefill is sharded by heads over 8 GPUs
+    torch = env[0]
+    host, dev_in, ns = inputs(env, 1, 4, 4096, 4096, True, seed=300 + d, D=d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = env[2].fa_fwd(*dev_in, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = [(0, h, i) for h in (0, 3) for i in (0, 127, 128, 1023, 1024, 2047, 2048, 3071, 3072, 4095)]
+    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, 4, 40), rng.integers(0, 4096, 40))]
+    O, L = oracle.attention_rows(*host, True, scale, rows)
+    idx = tuple(np.array(rows).T)
+    check(o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], O, L, f"head shard D={d} sampled rows ns={ns}")
