@@ -326,9 +326,13 @@ int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, floa
                      scale * fa::kLog2e, ws_o, ws_lse);
   int rc = launched("fa_fwd Split-D kernel launch");
   if (rc != FA_OK || ns == 1) return rc;
-  // combine the key parts of every query row: rows of [BH * Sq, ns, D]
-  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH * Sq), dim3(256), 0, stream, ws_o, ws_lse,
-                     static_cast<_Float16*>(o), lse, ns);
+  // combine the key parts of every query row: rows of [BH * Sq, ns, D], one
+  // tile of Sq rows per slice in the merge kernel's terms
+  const int64_t rows = (int64_t)BH * Sq;
+  if (rows > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  constexpr int R = fa::MergeCfg<D>::ROWS;
+  hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream, ws_o,
+                     ws_lse, static_cast<_Float16*>(o), lse, Sq, Sq, 0, 1, ns, (int)rows);
   return launched("fa_fwd Split-D merge launch");
 }
 
