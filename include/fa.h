@@ -84,10 +84,10 @@ enum fa_status {
  * slice of D, and their partial scores are summed through LDS.  When those
  * (query tile, slice) work items are fewer than the CUs, the Split-D key
  * range is also split and the parts merged with log-sum-exp weights
- * ("Split-KV" of the same list).  At D = 256, where one workgroup fills a
- * CU, a grid of at most two workgroups per CU whose heaviest (causal)
- * query tiles would leave most CUs idle near the end also has the key
- * ranges of those tiles split, when fa_fwd_key_splits() says it pays; a
+ * ("Split-KV" of the same list).  A grid of at most two query tiles per CU
+ * (D = 256; causal grids at D <= 128 too small for 256-row workgroups)
+ * whose heaviest query tiles would leave most CUs idle near the end has the
+ * key ranges of those tiles split, when fa_fwd_key_splits() says it pays; a
  * second kernel merges the parts.  Split calls keep their fp32 partials in
  * a per-device workspace that the library allocates on first need, grows
  * when a call needs more (after the previous call's kernels are done with
@@ -245,11 +245,14 @@ int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
  * heaviest query tiles of these sizes on a device with num_cus CUs (1: no
  * split), the same choice fa_fwd makes ("Adaptive High-Performance
  * Attention Kernels in CUDA", Split-K / Flash-Decoding, applied to prefill
- * query tiles).  D = 256: chosen by simulating the dispatch of the
- * work items (heaviest first, each to the CU that frees first) against the
- * cost of merging the parts.  D = 512, 1024: the Split-D key split (enough
- * parts to give every CU a work item when there are fewer than CUs, at most
- * 16).  D = 64, 128: 1.  Pure host arithmetic; returns 0 for invalid sizes.
+ * query tiles).  D = 256, and causal D = 64, 128 grids of 128-row
+ * workgroups (those with fewer 256-row tiles than CUs): chosen by
+ * simulating the dispatch of the work items (heaviest first, each to the
+ * CU that frees first) against the cost of merging the parts, with timing
+ * constants measured per kernel; at most 8 parts.  Other D = 64, 128 grids:
+ * 1.  D = 512, 1024: the Split-D key split (enough parts to give every CU a
+ * work item when there are fewer than CUs, at most 16).  Pure host
+ * arithmetic; returns 0 for invalid sizes.
  */
 int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
 
