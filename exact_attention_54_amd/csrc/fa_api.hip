@@ -54,8 +54,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d Sq=%d Sk=%d D=%d)", B, H, Sq, Sk, D);
-  if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024)
-    return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256, 512, 1024}", D);
+  if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512 && D != 1024)
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128, 256, 512, 1024}", D);
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
@@ -268,6 +268,9 @@ int launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, hipStream_t stream) {
   if constexpr (D == 256) {
     return launch_fwd<256, 32, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+  } else if constexpr (D == 32) {
+    // a 64-key tile of D = 32 is 4 KiB: one 1 KiB copy for each of 4 wavefronts
+    return launch_fwd<32, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
   } else {
     int cus = 0;
     int rc = device_cu_count(&cus);
@@ -298,6 +301,8 @@ int launch_fwd_varlen_d(const void* q, const void* k, const void* v, void* o, fl
                         float scale, hipStream_t stream) {
   if constexpr (D == 256) {
     return launch_fwd_varlen<256, 32, 4, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
+  } else if constexpr (D == 32) {
+    return launch_fwd_varlen<32, 64, 4, CAUSAL>(q, k, v, o, lse, va, B, scale, stream);
   } else {
     int cus = 0;
     int rc = device_cu_count(&cus);
@@ -571,7 +576,7 @@ int validate_decode(const void* q, const void* k, const void* v, const void* o, 
                     int Sq, int Sk, int D, int causal, float scale, int num_splits) {
   int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
   if (rc != FA_OK) return rc;
-  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "split-KV decoding supports head dims 64, 128, 256");
+  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "split-KV decoding supports head dims 32, 64, 128, 256");
   if (Sq != 1) return fail(FA_ERR_INVALID_ARG, "split-KV decoding needs Sq == 1 (got %d)", Sq);
   if (causal != 0) return fail(FA_ERR_INVALID_ARG, "split-KV decoding is non-causal");
   if (num_splits > Sk) return fail(FA_ERR_INVALID_ARG, "num_splits %d exceeds Sk %d", num_splits, Sk);
@@ -584,6 +589,7 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   float* ws_o = static_cast<float*>(ws);  // unused (may be null) with a single partition
   float* ws_lse = ws ? ws_o + (size_t)BH * ns * D : nullptr;
   switch (D) {
+    case 32: return launch_decode<32>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
     case 64: return launch_decode<64>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
     case 128: return launch_decode<128>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
     default: return launch_decode<256>(q, k, v, o, lse, BH, Sk, scale, stream, ns, ws_o, ws_lse);
@@ -597,7 +603,8 @@ int validate_varlen(const void* q, const void* k, const void* v, const void* o, 
   if (B < 1 || H < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d total_q=%d total_k=%d max_q=%d max_k=%d D=%d)",
                 B, H, total_q, total_k, max_q, max_k, D);
-  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128, 256}", D);
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
@@ -621,7 +628,8 @@ int validate_paged(const void* q, const void* kc, const void* vc, const int* tab
   if (B < 1 || H < 1 || D < 1 || num_blocks < 1 || max_blocks < 1)
     return fail(FA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d D=%d num_blocks=%d max_blocks=%d)", B, H, D,
                 num_blocks, max_blocks);
-  if (D != 64 && D != 128 && D != 256) return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {64, 128, 256}", D);
+  if (D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128, 256}", D);
   if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
     return fail(FA_ERR_INVALID_ARG, "block_size %d is not a power of two in [1, 1024]", block_size);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -668,6 +676,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
+    case 32:
+      return causal ? launch_fwd_d<32, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
+                    : launch_fwd_d<32, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
     case 64:
       return causal ? launch_fwd_d<64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
                     : launch_fwd_d<64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
@@ -693,6 +704,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   fa::VarlenArgs va = {cu_seqlens_q, cu_seqlens_k, H, total_q, total_k, max_seqlen_q, max_seqlen_k};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
+    case 32:
+      return causal ? launch_fwd_varlen_d<32, true>(q, k, v, o, lse, va, B, scale, s)
+                    : launch_fwd_varlen_d<32, false>(q, k, v, o, lse, va, B, scale, s);
     case 64:
       return causal ? launch_fwd_varlen_d<64, true>(q, k, v, o, lse, va, B, scale, s)
                     : launch_fwd_varlen_d<64, false>(q, k, v, o, lse, va, B, scale, s);
@@ -740,10 +754,11 @@ int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_c
   if ((int64_t)B * H > kMaxGrid) return 0;
   const int BH = B * H;
   switch (D) {
+    case 32:
     case 64:
     case 128: {
       // the 8-wavefront kernel (grids that give every CU a workgroup) is never split
-      if ((int64_t)BH * ((Sq + 255) / 256) >= num_cus) return 1;
+      if (D != 32 && (int64_t)BH * ((Sq + 255) / 256) >= num_cus) return 1;
       using Cfg = fa::FwdCfg<128, 64, 4>;
       const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
       return plan_fwd_split(nqt, BH, Cfg::BM, 64, D, Sq, Sk, causal != 0, num_cus).ns;
@@ -840,6 +855,10 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
   float* ws_o = static_cast<float*>(ws);
   float* ws_lse = ws ? ws_o + (size_t)B * H * ns * D : nullptr;
   switch (D) {
+    case 32:
+      rc = launch_decode_paged<32>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
+                                   max_blocks, scale, s, ns, ws_o, ws_lse);
+      break;
     case 64:
       rc = launch_decode_paged<64>(q, k_cache, v_cache, block_tables, seq_lens, o, lse, B, H, num_blocks, lbs,
                                    max_blocks, scale, s, ns, ws_o, ws_lse);

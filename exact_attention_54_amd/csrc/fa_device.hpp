@@ -71,11 +71,14 @@ __device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
 // Row-major [key][d] layout for V tiles read with ds_read_b64_tr_b16: a
 // transposed read touches 4 consecutive key rows x 4 consecutive 16-byte
 // chunks, and the XOR below spreads those 16 chunks over the 16 bank groups
-// of a 256-byte line.
+// of a 256-byte line.  With 4 chunks per row (D = 32) those 4 rows are one
+// whole line already.
 template <int C>
 __device__ __forceinline__ uint32_t vswz(int r, int c) {
-  static_assert(C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
-  if constexpr (C >= 16) {
+  static_assert(C == 4 || C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
+  if constexpr (C == 4) {
+    return (uint32_t)(r * 64 + c * 16);
+  } else if constexpr (C >= 16) {
     const int line = r * (C / 16) + (c >> 4);
     const int slot = (c & 15) ^ (4 * (r & 3));
     return (uint32_t)(line * 256 + slot * 16);
@@ -87,7 +90,10 @@ __device__ __forceinline__ uint32_t vswz(int r, int c) {
 }
 template <int C>
 __device__ __forceinline__ void vswz_inv(int line, int slot, int& r, int& c) {
-  if constexpr (C >= 16) {
+  if constexpr (C == 4) {
+    r = line * 4 + slot / 4;
+    c = slot % 4;
+  } else if constexpr (C >= 16) {
     r = line / (C / 16);
     c = (line % (C / 16)) * 16 + (slot ^ (4 * (r & 3)));
   } else {

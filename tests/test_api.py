@@ -61,7 +61,7 @@ def dec_ws(lib, ws=A + 0x8000, nbytes=1 << 20, p=P, ns=2, **kw):
     (dict(Sk=0), _capi.FA_ERR_INVALID_ARG),
     (dict(D=0), _capi.FA_ERR_INVALID_ARG),
     (dict(D=96), _capi.FA_ERR_UNSUPPORTED),
-    (dict(D=32), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=16), _capi.FA_ERR_UNSUPPORTED),
     (dict(D=2048), _capi.FA_ERR_UNSUPPORTED),
     (dict(D=384), _capi.FA_ERR_UNSUPPORTED),
     (dict(causal=2), _capi.FA_ERR_INVALID_ARG),
@@ -150,6 +150,7 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
     (1, 4, 4096, 4096, 128, 1, 256, 3),    # one GPU's 4 heads of it: 128 tiles, heaviest 32x the lightest
     (1, 2, 8192, 8192, 128, 1, 256, 4),
     (1, 1, 4096, 4096, 64, 1, 256, 4),
+    (8, 16, 2048, 2048, 32, 1, 256, 1),    # D = 32 (always 128-row workgroups): 2048 tiles
     (1, 8, 2048, 2048, 128, 0, 256, 1),    # D <= 128 non-causal: measured no gain, never split
     (2, 8, 1024, 1024, 128, 1, 256, 1),    # short tiles: the merge costs what the balance saves
     (1, 16, 2048, 2048, 256, 1, 256, 1),   # 256 tiles, one per CU: the merge would cost about what it saves
@@ -259,7 +260,7 @@ def paged(lib, p=P, t=TBL, **kw):
     (dict(block_size=0), _capi.FA_ERR_INVALID_ARG),
     (dict(block_size=12), _capi.FA_ERR_INVALID_ARG),     # not a power of two
     (dict(block_size=2048), _capi.FA_ERR_INVALID_ARG),   # above 1024
-    (dict(D=32), _capi.FA_ERR_UNSUPPORTED),
+    (dict(D=16), _capi.FA_ERR_UNSUPPORTED),
     (dict(scale=-1.0), _capi.FA_ERR_INVALID_ARG),
     (dict(ns=65), _capi.FA_ERR_INVALID_ARG),             # more splits than the table reaches (4 * 16)
     (dict(max_blocks=1 << 21, block_size=1024), _capi.FA_ERR_INVALID_ARG),

@@ -126,7 +126,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_prefill(torch_dev, fa, D, shape, causal):
@@ -168,7 +168,7 @@ def test_other_scales_and_large_scores(torch_dev, fa, scale):
         assert_close(o, lse, O, L, f"scale={scale} causal={causal}")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_closed_forms_on_gpu(torch_dev, fa, D):
     B, H, S = 1, 2, 150
     _, k, v = make_qkv(B, H, S, S, D, seed=5)
@@ -192,7 +192,7 @@ def test_closed_forms_on_gpu(torch_dev, fa, D):
 
 # ------------------------------------------------------------------ decode
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 64, 0])
 def test_decode_split_sweep(torch_dev, fa, D, ns):
     B, H, Sk = 2, 4, 8191

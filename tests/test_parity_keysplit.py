@@ -146,6 +146,7 @@ SPLIT_SMALL_D = [
     (1, 1, 3000, 1000, 128),    # more queries than keys
     (1, 2, 1000, 1000, 64),
     (1, 2, 2000, 2000, 64),
+    (1, 2, 2000, 2000, 32),
 ]
 
 

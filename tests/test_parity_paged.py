@@ -77,7 +77,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("cs", CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}bs{c[3]}" for c in CASES])
 @pytest.mark.parametrize("ns", [0, 1, 3, 8])
 def test_paged_parity(torch_dev, fa, D, cs, ns):

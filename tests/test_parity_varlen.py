@@ -79,7 +79,7 @@ BATCHES = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("bt", BATCHES, ids=[f"b{i}" for i in range(len(BATCHES))])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_parity(torch_dev, fa, D, bt, causal):
