@@ -71,7 +71,7 @@ enum fa_status {
  *
  *   q      [B, H, Sq, D] fp16        k, v  [B, H, Sk, D] fp16
  *   o      [B, H, Sq, D] fp16 out    lse   [B, H, Sq]    fp32 out
- *   B, H, Sq, Sk >= 1;  D in {64, 128, 256, 512, 1024};  causal 0 or 1;
+ *   B, H, Sq, Sk >= 1;  D in {32, 64, 128, 256, 512, 1024};  causal 0 or 1;
  *   scale > 0.
  *
  * Queries are split into tiles, one workgroup each ("Split-Q" in
@@ -116,7 +116,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * overlap inputs.  A per-row workspace (D and the LSE in log2 units,
  * 2*B*H*Sq fp32) comes from the same
  * per-device pool as fa_decode_splitkv.  Four kernels run on `stream`.
- * Supports D in {64, 128} (D = 256: FA_ERR_UNSUPPORTED); other errors as
+ * Supports D in {64, 128} (other D: FA_ERR_UNSUPPORTED); other errors as
  * fa_fwd.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -144,6 +144,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * [0, min(total - start, max_seqlen)], so nothing outside the tensors is
  * read or written.  Query rows that no sequence covers are left untouched;
  * a query row whose sequence has no key gets o = 0 and lse = -inf.
+ * D in {32, 64, 128, 256} (other D: FA_ERR_UNSUPPORTED).
  * Limits: (max_seqlen + 256) * H * D * 2 < 2^31 bytes for q and for k.
  * Errors as fa_fwd.
  */
@@ -158,7 +159,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * Kernels in CUDA", Advanced Production Features, 1. Split-K FlashDecoding).
  *
  * Same arguments as fa_fwd plus num_splits; requires Sq == 1 and causal == 0
- * (FA_ERR_INVALID_ARG otherwise) and D in {64, 128, 256}
+ * (FA_ERR_INVALID_ARG otherwise) and D in {32, 64, 128, 256}
  * (FA_ERR_UNSUPPORTED otherwise).  Partition s covers keys
  * [s*c, min((s+1)*c, Sk)) with c = ceil(Sk / num_splits); trailing
  * partitions may be empty.  num_splits <= 0 picks fa_decode_auto_splits()
@@ -223,7 +224,7 @@ int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, f
  * block_size, CUs); otherwise 1 <= num_splits <= max_blocks * block_size.
  * Workspace, pool and stream behaviour as fa_decode_splitkv.  Returns
  * FA_ERR_INVALID_ARG for null / misaligned pointers or bad sizes,
- * FA_ERR_UNSUPPORTED for D not in {64, 128, 256}.
+ * FA_ERR_UNSUPPORTED for D not in {32, 64, 128, 256}.
  */
 int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                     const int* block_tables, const int* seq_lens, void* o, float* lse,
@@ -245,7 +246,7 @@ int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
  * heaviest query tiles of these sizes on a device with num_cus CUs (1: no
  * split), the same choice fa_fwd makes ("Adaptive High-Performance
  * Attention Kernels in CUDA", Split-K / Flash-Decoding, applied to prefill
- * query tiles).  D = 256, and causal D = 64, 128 grids of 128-row
+ * query tiles).  D = 256, and causal D = 32, 64, 128 grids of 128-row
  * workgroups (those with fewer 256-row tiles than CUs): chosen by
  * simulating the dispatch of the work items (heaviest first, each to the
  * CU that frees first) against the cost of merging the parts, with timing
