@@ -102,8 +102,9 @@ def test_paged_long_partition_segments(torch_dev, fa):
 
 
 @pytest.mark.parametrize("ns", [0, 1, 3])   # 1: the single-kernel form merges in LDS
-def test_paged_absent_and_out_of_range_pages(torch_dev, fa, ns):
-    B, H, S, D, bs = 3, 2, 96, 64, 16
+@pytest.mark.parametrize("D", [64, 128])     # 16-token pages: 2 and 1 pages per wavefront iteration
+def test_paged_absent_and_out_of_range_pages(torch_dev, fa, ns, D):
+    B, H, S, bs = 3, 2, 96, 16
     q, kc, vc, tables = case(B, H, S, D, bs, 41)
     tables = tables.copy()
     tables[0, 1] = -1
