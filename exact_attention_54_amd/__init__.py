@@ -81,6 +81,12 @@ def _outputs(q, o, lse):
 def _stream(q, stream):
     torch = _torch()
     if stream is None:
+        # the current stream's handle without building a Stream object
+        # (~0.1 us against ~2 us, which dominated the host cost of a call)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            idx = q.device.index
+            return raw(torch.cuda.current_device() if idx is None else idx)
         stream = torch.cuda.current_stream(q.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
