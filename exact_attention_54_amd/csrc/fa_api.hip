@@ -345,6 +345,17 @@ int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, floa
 // the final output; no workspace, no merge kernel).
 constexpr int kDecFusedThreads = 1024;
 
+// Phase two of the split decode: 1024-thread merge workgroups when 256
+// threads would leave each partition group more than 4 partitions.
+template <int D>
+void launch_decode_merge(int BH, int ns, hipStream_t stream, const float* ws_o, const float* ws_lse, _Float16* o,
+                         float* lse) {
+  if (ns > 4 * fa::DecMergeCfg<D, 256>::G)
+    hipLaunchKernelGGL((fa::decode_merge_kernel<D, 1024>), dim3(BH), dim3(1024), 0, stream, ws_o, ws_lse, o, lse, ns);
+  else
+    hipLaunchKernelGGL((fa::decode_merge_kernel<D, 256>), dim3(BH), dim3(256), 0, stream, ws_o, ws_lse, o, lse, ns);
+}
+
 template <int D>
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sk,
                   float scale, hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
@@ -362,8 +373,7 @@ int launch_decode(const void* q, const void* k, const void* v, void* o, float* l
                      static_cast<const _Float16*>(v), ws_o, ws_lse, nullptr, nullptr, Sk, ns, chunk, c2);
   int rc = launched("decode phase-one launch");
   if (rc != FA_OK) return rc;
-  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
-                     static_cast<_Float16*>(o), lse, ns);
+  launch_decode_merge<D>(BH, ns, stream, ws_o, ws_lse, static_cast<_Float16*>(o), lse);
   return launched("decode merge launch");
 }
 
@@ -386,8 +396,7 @@ int launch_decode_paged(const void* q, const void* kc, const void* vc, const int
                      num_blocks, lbs, max_blocks, c2);
   int rc = launched("paged decode phase-one launch");
   if (rc != FA_OK) return rc;
-  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(BH), dim3(D), 0, stream, ws_o, ws_lse,
-                     static_cast<_Float16*>(o), lse, ns);
+  launch_decode_merge<D>(BH, ns, stream, ws_o, ws_lse, static_cast<_Float16*>(o), lse);
   return launched("paged decode merge launch");
 }
 

@@ -313,29 +313,73 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
   decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256)
+// Phase two: one workgroup of T threads per slice.  D/4 threads cover a row
+// (4 consecutive d each, 16-byte loads), so the workgroup holds G = 4T/D
+// such groups; group g takes partitions g, g + G, g + 2G, ..., and the G
+// group sums are added through LDS in group order (deterministic for a
+// given ns and T).  Spreading the partitions over the workgroup keeps a
+// slice's merge short when a small batch is split into many partitions:
+// 256 threads, or 1024 when that leaves a group more than 4 partitions.
+template <int D, int T = 256>
+struct DecMergeCfg {
+  static constexpr int TPR = D / 4;     // threads per row
+  static constexpr int G = T / TPR;     // partition groups
+  static_assert(D % 4 == 0 && T % TPR == 0 && G >= 1, "merge geometry");
+};
+
+template <int D, int T>
+__global__ void __launch_bounds__(T)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     _Float16* __restrict__ O, float* __restrict__ LSE, int ns) {
+  using M = DecMergeCfg<D, T>;
+  __shared__ __attribute__((aligned(16))) float s_num[M::G][D];
+  __shared__ float s_den[M::G];
+  __shared__ float s_max[M::G];
   const int bh = blockIdx.x;
+  const int g = (int)threadIdx.x / M::TPR;
+  const int d0 = 4 * ((int)threadIdx.x % M::TPR);
   const float* lp = ws_lse + (size_t)bh * ns;
-  const float* op = ws_o + (size_t)bh * ns * D;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lp[s]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    if (M == kNegInf) {  // no key at all (empty paged context): O = 0, LSE = -inf
-      O[(size_t)bh * D + d] = (_Float16)0.f;
-      if (d == 0) LSE[bh] = kNegInf;
-      continue;
+  const float* op = ws_o + (size_t)bh * ns * D + d0;
+  // lse max over the partitions: per group, then across the groups
+  float mx = kNegInf;
+  for (int s = g; s < ns; s += M::G) mx = fmaxf(mx, lp[s]);
+  if (d0 == 0) s_max[g] = mx;
+  __syncthreads();
+  mx = s_max[0];
+#pragma unroll
+  for (int j = 1; j < M::G; ++j) mx = fmaxf(mx, s_max[j]);
+  if (mx == kNegInf) {  // no key at all (empty paged context): O = 0, LSE = -inf
+    if (g == 0) {
+      *reinterpret_cast<h4*>(O + (size_t)bh * D + d0) = h4{0, 0, 0, 0};
+      if (d0 == 0) LSE[bh] = kNegInf;
     }
-    float den = 0.f, num = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float wgt = exp2_fast((lp[s] - M) * kLog2e);
-      den += wgt;
-      num += wgt * op[(size_t)s * D + d];
+    return;
+  }
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int s = g; s < ns; s += M::G) {
+    const float wgt = exp2_fast((lp[s] - mx) * kLog2e);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(op + (size_t)s * D);
+    den += wgt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] += wgt * x[e];
+  }
+  *reinterpret_cast<f32x4*>(&s_num[g][d0]) = num;
+  if (d0 == 0) s_den[g] = den;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int j = 1; j < M::G; ++j) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&s_num[j][d0]);
+      den += s_den[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += x[e];
     }
-    O[(size_t)bh * D + d] = (_Float16)(num / den);
-    if (d == 0) LSE[bh] = M + __builtin_logf(den);
+    h4 res;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = (_Float16)(num[e] / den);
+    *reinterpret_cast<h4*>(O + (size_t)bh * D + d0) = res;
+    if (d0 == 0) LSE[bh] = mx + __builtin_logf(den);
   }
 }
 
