@@ -414,6 +414,29 @@ def main():
     tflops_d256 = prefill_flops(w5.B, w5.H, w5.Sq, w5.Sk, w5.D, True) / t_d256 / 1e12
     log(f"D=256 causal prefill (1,16,2048,2048,256): {t_d256 * 1e6:.1f} us = {tflops_d256:.1f} TFLOPS")
 
+    # Batch-1 decoding (one sequence, as a latency-bound server step): 32
+    # heads over 8K keys and 8 heads over 32K keys, the library's split
+    # choice, two kernels (partitions, then their merge) per call.
+    small_dec = {}
+    for sb, sh, ssk in ((1, 32, 8192), (1, 8, 32768)):
+        qb, kb_, vb_ = (torch.from_numpy(x).to(dev) for x in make_qkv(sb, sh, 1, ssk, 128, seed=40 + sh))
+        ob = torch.empty_like(qb)
+        lb = torch.empty((sb, sh, 1), dtype=torch.float32, device=dev)
+
+        def dec1(qb=qb, kb_=kb_, vb_=vb_, ob=ob, lb=lb):
+            fa.fa_decode_splitkv(qb, kb_, vb_, ob, lb, scale=128 ** -0.5)
+
+        for _ in range(max(args.warmup, 3)):
+            dec1()
+        t_b = time_launches(torch, dec1, args.steps)
+        tag = f"decode_b{sb}_h{sh}_k{ssk // 1024}k"
+        small_dec[tag + "_us"] = round(t_b * 1e6, 2)
+        small_dec[tag + "_gbps"] = round(2 * sb * sh * ssk * 128 * 2 / t_b / 1e9, 1)
+        small_dec[tag + "_splits"] = fa.fa_decode_auto_splits(sb, sh, ssk, cus)
+        log(f"batch-1 decode ({sb},{sh},1,{ssk},128): {t_b * 1e6:.1f} us = {small_dec[tag + '_gbps']} GB/s "
+            f"({small_dec[tag + '_splits']} partitions)")
+        del qb, kb_, vb_, ob, lb
+
     # One GPU's share of the LLaMA-7B-shaped prefill sharded by heads over 8
     # GPUs: 4 of the 32 heads, (1, 4, 4096, 4096, 128) causal.  128 query
     # tiles leave most CUs idle, so fa_fwd splits the key ranges of the
@@ -545,6 +568,7 @@ def main():
             "head_shard_prefill_frac_of_peak": round(tflops_shard / PEAK_FP16_TFLOPS, 4),
             "head_shard_prefill_us": round(t_shard * 1e6, 2),
             "head_shard_key_parts": shard_parts,
+            **small_dec,
             **small,
             **context,
             **{"splitd_" + k: x for k, x in splitd.items()},
