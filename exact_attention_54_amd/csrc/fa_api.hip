@@ -681,6 +681,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int causal, float scale, void* stream) {
   int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
   if (rc != FA_OK) return rc;
+  // a single query row attending to every key is a decode step: the split-KV
+  // path ("FlashAttention-2 MMA", Architecture & Dispatch Flow, seq_q == 1).
+  // Causal single rows see key 0 only (top-left mask) and stay on Split-Q.
+  if (Sq == 1 && causal == 0 && D <= 256)
+    return fa_decode_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, 0, scale, stream, 0);
   const int BH = B * H;
   if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);

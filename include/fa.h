@@ -94,7 +94,11 @@ enum fa_status {
  * it) and keeps until the process ends; a call on another stream than the
  * previous split call first waits on the GPU for that call's kernels, so
  * split calls on one device run one after another.
- * Any Sq works, including Sq = 1.  o and lse must not overlap the inputs.
+ * Any Sq works.  A non-causal call with Sq = 1 and D <= 256 is a decode step
+ * and runs fa_decode_splitkv with the automatic split count (the page's
+ * dispatch of seq_q == 1 to Split-KV); with causal = 1 a single row sees
+ * key 0 only and stays on the prefill kernel.  o and lse must not overlap
+ * the inputs.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Sq, int Sk, int D, int causal, float scale,

@@ -203,6 +203,24 @@ def test_decode_split_sweep(torch_dev, fa, D, ns):
     assert_close(o, lse, O, L, f"decode D={D} ns={ns}")
 
 
+def test_fwd_single_query_runs_the_decode(torch_dev, fa):
+    # fa_fwd with Sq = 1, non-causal: the split-KV decode (bitwise the same
+    # result as fa_decode_splitkv), here over a long context with few heads
+    torch, _ = torch_dev
+    q, k, v = make_qkv(1, 2, 1, 50000, 128, seed=71)
+    qd, kd, vd = to_dev(torch_dev, q, k, v)
+    o1, l1 = fa.fa_fwd(qd, kd, vd, causal=False)
+    o2, l2 = fa.fa_decode_splitkv(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    O, L = oracle.attention(q, k, v, False, 1.0 / math.sqrt(128))
+    assert_close(o1.float().cpu().numpy(), l1.cpu().numpy(), O, L, "fa_fwd Sq=1")
+    # causal Sq = 1 sees key 0 only (top-left mask): O = V[0]
+    o3, l3 = fa.fa_fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o3.float().cpu().numpy()[:, :, 0], v[:, :, 0].astype(np.float32))
+
+
 @pytest.mark.parametrize("Sk,ns", [(1, 1), (5, 5), (100, 64), (300, 0), (1000, 999)])
 def test_decode_small_and_empty_partitions(torch_dev, fa, Sk, ns):
     q, k, v = make_qkv(3, 2, 1, Sk, 128, seed=Sk)
