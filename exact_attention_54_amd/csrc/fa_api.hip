@@ -453,7 +453,7 @@ int device_cu_count(int* out) {
 
 // One stream-ordered memory pool per device for decode workspaces.  Its
 // release threshold is unlimited, so memory freed with hipFreeAsync stays in
-// the pool and the next call reuses it without going back to the driver.
+// the pool and the next call reuses it without a new device allocation.
 constexpr int kMaxDevices = 64;
 std::mutex g_pool_mu;
 hipMemPool_t g_pool[kMaxDevices] = {};
