@@ -181,6 +181,29 @@ def test_fwd_key_splits_stays_within_sensible_bounds(lib):
             assert ns == 1
 
 
+def test_fwd_key_splits_properties_on_random_shapes(lib):
+    # invariants of the split choice over 2000 seeded shapes: parts in 1..8
+    # (D <= 256) or 1..16 (Split-D); non-causal D <= 128 grids and grids
+    # with a 256-row tile per CU are never split; invalid sizes give 0
+    import numpy as np
+
+    g = np.random.Generator(np.random.PCG64(5))
+    for _ in range(2000):
+        B, H = int(g.integers(1, 5)), int(g.integers(1, 65))
+        Sq, Sk = int(g.integers(1, 20000)), int(g.integers(1, 20000))
+        D = int(g.choice([32, 64, 128, 256, 512, 1024]))
+        causal = int(g.integers(0, 2))
+        cus = int(g.choice([80, 256, 304]))
+        ns = lib.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus)
+        assert 1 <= ns <= (16 if D >= 512 else 8), (B, H, Sq, Sk, D, causal, cus, ns)
+        if D in (64, 128) and (not causal or B * H * -(-Sq // 256) >= cus):
+            assert ns == 1, (B, H, Sq, Sk, D, causal, cus, ns)
+        if D <= 256 and B * H * -(-Sq // 128) > 2 * cus:
+            assert ns == 1, (B, H, Sq, Sk, D, causal, cus, ns)
+    assert lib.fa_fwd_key_splits(1, 1, 0, 5, 128, 1, 256) == 0
+    assert lib.fa_fwd_key_splits(1, 1, 5, 5, 48, 1, 256) == 0
+
+
 def test_status_strings(lib):
     assert _capi.status_name(0) == "ok"
     assert _capi.status_name(1) == "invalid argument"
