@@ -178,6 +178,19 @@ def test_paged_8k_sampled_against_oracle(torch_dev, fa, paged_8k):
         check(o[b : b + 1, h : h + 1], lse[b : b + 1, h : h + 1], O, L, f"8k paged b={b} h={h}")
 
 
+@pytest.mark.parametrize("D", [32, 128, 256])
+def test_paged_many_partitions(torch_dev, fa, D):
+    # 64 partitions per slice: the merge runs its 1024-thread form (more
+    # than 4 partitions per group at 256 threads for D >= 64)
+    B, H, S, bs = 2, 3, 3000, 16
+    q, kc, vc, tables = case(B, H, S, D, bs, 71 + D)
+    seq_lens = np.array([3000, 1777], dtype=np.int32)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = gpu_paged(torch_dev, fa, q, kc, vc, tables, seq_lens, scale, 64)
+    O, L = oracle.decode_paged(q, kc, vc, tables, seq_lens, scale)
+    check(o, lse, O, L, f"paged D={D} ns=64")
+
+
 def test_paged_bitwise_repeatable(torch_dev, fa):
     torch, _ = torch_dev
     q, kc, vc, tables = case(2, 3, 500, 128, 16, 61)
