@@ -33,6 +33,9 @@
  *   Stream    `stream` is a hipStream_t passed as void* (NULL = the null
  *             stream).  Every call only enqueues work on that stream and
  *             returns; results are valid once the stream has reached them.
+ *             (One exception: a key-split fa_fwd call that needs a larger
+ *             forward workspace first waits, on the host, for the previous
+ *             key-split call's kernels; see fa_fwd.)
  *   Causal    top-left aligned: query row i sees keys 0..i (all keys when
  *             i >= Sk), so no row is ever fully masked.
  *   Scale     any finite scale > 0 (the pages use 1/sqrt(D)).
