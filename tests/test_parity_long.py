@@ -68,3 +68,18 @@ def test_prefill_256k_keys(torch_dev, fa, causal):
     torch.cuda.synchronize()
     O, L = oracle.attention(q, k, v, causal, 0.3)
     check(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, f"prefill 130 x 2^18 keys causal={causal}")
+
+
+def test_prefill_128k_keys_key_split(torch_dev, fa):
+    # D = 256, 130 queries over 2^17 keys: two query tiles on a whole GPU,
+    # so fa_fwd splits each key range (up to 8 parts of ~500 key tiles) and
+    # merges them; part offsets reach tens of MiB inside the slice
+    torch, dev = torch_dev
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert fa.fa_fwd_key_splits(1, 1, 130, 1 << 17, 256, False, cus) > 1
+    q, k, v = make_qkv(1, 1, 130, 1 << 17, 256, seed=63)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=False, scale=0.25)  # peaky: O of order one
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, False, 0.25)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, "prefill D=256 130 x 2^17 keys, key split")
