@@ -294,6 +294,28 @@ def test_side_stream(torch_dev, fa):
     assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, "side stream")
 
 
+def test_split_decodes_on_two_streams_and_growth(torch_dev, fa):
+    # split decodes share one workspace per device: queued back to back on
+    # two streams (each waits on the GPU for the other's previous call), the
+    # second size larger than the first (the workspace grows in between)
+    torch, dev = torch_dev
+    cases = [make_qkv(1, 4, 1, 3000, 128, seed=81), make_qkv(2, 6, 1, 9000, 64, seed=82)]
+    dev_in = [to_dev(torch_dev, *c) for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]  # default priority
+    outs = []
+    for rep in range(3):
+        for i, (qd, kd, vd) in enumerate(dev_in):
+            with torch.cuda.stream(streams[i]):
+                outs.append((i, fa.fa_decode_splitkv(qd, kd, vd, num_splits=16 + 8 * rep)))
+    for st in streams:
+        st.synchronize()
+    for n, (i, (o, lse)) in enumerate(outs):
+        q, k, v = cases[i]
+        O, L = oracle.attention(q, k, v, False, 1.0 / math.sqrt(q.shape[-1]))
+        assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, f"decode stream {i} call {n}")
+
+
 def test_errors_raise(torch_dev, fa):
     torch, dev = torch_dev
     q = torch.zeros(1, 1, 2, 128, dtype=torch.float16, device=dev)
