@@ -114,8 +114,9 @@ struct SplitPlan {
 // and merge, rocprofv3 kernel trace):
 //   D = 256, one workgroup per CU: seven plans of the (1, 16, 2048, 2048)
 //     causal shape, all within 6%;
-//   D <= 128, the 4-wavefront kernel: 34 plans over five shapes, within 26%,
-//     with every split decision right.
+//   D <= 128, the 4-wavefront kernel: 34 plans over five shapes; with
+//     these constants every shape gets its fastest measured plan or one
+//     within 1% of it (and the shapes where no split paid stay whole).
 // A work item costs its key tiles at unit_us each plus item_us of fixed
 // work (Q load, pipeline fill, epilogue); items go, heaviest first, to the
 // CU that frees first; and the whole job takes at least full_load times its
@@ -129,8 +130,8 @@ struct SplitModel {
 SplitModel fwd_split_model(int D) {
   if (D == 256) return {4.0 * 128 * 32 * 256 / 3.2e6, 3.9, 1.5, 0.9, false};
   // a lone 4-wavefront workgroup of 128 rows runs a 64-key tile of D = 128
-  // in ~1.1 us; non-causal grids measured no gain from splitting
-  return {1.1 * D / 128.0, 6.6, 1.0, 0.8, true};
+  // in ~1.2 us; non-causal grids measured no gain from splitting
+  return {1.2 * D / 128.0, 3.0, 1.0, 0.7, true};
 }
 
 double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots,

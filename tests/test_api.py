@@ -147,7 +147,7 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
 
 @pytest.mark.parametrize("B,H,Sq,Sk,D,causal,cus,want", [
     (1, 32, 4096, 4096, 128, 1, 256, 1),   # 8-wavefront grid (every CU has a workgroup): never split
-    (1, 4, 4096, 4096, 128, 1, 256, 3),    # one GPU's 4 heads of it: 128 tiles, heaviest 32x the lightest
+    (1, 4, 4096, 4096, 128, 1, 256, 4),    # one GPU's 4 heads of it: 128 tiles, heaviest 32x the lightest
     (1, 2, 8192, 8192, 128, 1, 256, 4),
     (1, 1, 4096, 4096, 64, 1, 256, 4),
     (8, 16, 2048, 2048, 32, 1, 256, 1),    # D = 32 (always 128-row workgroups): 2048 tiles
