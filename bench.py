@@ -26,6 +26,12 @@ import os
 import sys
 import time
 
+# The oracle's BLAS uses every core this process may run on, fixed before
+# numpy is first imported (an explicit setting in the environment is kept).
+AFFINITY_CORES = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(AFFINITY_CORES))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -150,7 +156,7 @@ def roofline_context(torch, dev, buf, cus, warmup):
     """Times the plain read-stream and MFMA-loop probes (HIP events)."""
     import ctypes
 
-    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hip", "libroofline_probe.so"))
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_54_amd", "libroofline_probe.so"))
     lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     st = torch.cuda.current_stream(dev).cuda_stream
@@ -183,41 +189,79 @@ def blas_threads():
             return max(n)
     except Exception:
         pass
-    return len(os.sched_getaffinity(0))
+    return int(os.environ.get("OPENBLAS_NUM_THREADS", AFFINITY_CORES))
 
 
-def cpu_baseline(pre, dec, budget_s=20.0):
-    """The fp64 oracle timed on a bounded sample of the same two workloads."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def median_time(fn, single_run_s=10.0):
+    """Wall time of fn(): one run if it takes at least single_run_s, else the
+    median of three."""
+    t0 = time.perf_counter()
+    fn()
+    t = [time.perf_counter() - t0]
+    if t[0] < single_run_s:
+        for _ in range(2):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+    return sorted(t)[len(t) // 2], len(t)
+
+
+def cpu_baseline(pre, dec, budget_s=10.0):
+    """The fp64 oracle timed on a bounded sample of the same two workloads:
+    whole (b, h) slices of the prefill and whole batch entries of the decode,
+    as many as one run of about budget_s allows.  The fp16 -> fp64 widening
+    happens before the timer; each figure is the median of three runs (one
+    run if it takes over 10 s)."""
+    import numpy as np
+
     import oracle
 
     (w3, q3, k3, v3), (w4, q4, k4, v4) = pre, dec
-    # prefill: whole (b, h) slices of the causal workload, as many as fit half the budget
-    heads, t_pre = 0, 0.0
-    while heads < w3.H and t_pre < budget_s / 2:
-        h = heads
-        t0 = time.perf_counter()
-        oracle.attention(q3[:, h : h + 1], k3[:, h : h + 1], v3[:, h : h + 1], True, w3.scale)
-        t_pre += time.perf_counter() - t0
-        heads += 1
+    # prefill: the first `heads` heads, sized from the time of one head
+    q64, k64, v64 = (np.ascontiguousarray(x, dtype=np.float64) for x in (q3, k3, v3))
+    t0 = time.perf_counter()
+    oracle.attention(q64[:, :1], k64[:, :1], v64[:, :1], True, w3.scale)
+    heads = max(1, min(w3.H, int(budget_s / max(time.perf_counter() - t0, 1e-6))))
+    t_pre, runs_pre = median_time(
+        lambda: oracle.attention(q64[:, :heads], k64[:, :heads], v64[:, :heads], True, w3.scale))
+    del q64, k64, v64
     pre_tflops = prefill_flops(1, heads, w3.Sq, w3.Sk, w3.D, True) / t_pre / 1e12
-    # decode: whole batch entries of the decode workload
-    nb, t_dec = 0, 0.0
-    while nb < w4.B and t_dec < budget_s / 2:
-        t0 = time.perf_counter()
-        oracle.attention(q4[nb : nb + 1], k4[nb : nb + 1], v4[nb : nb + 1], False, w4.scale)
-        t_dec += time.perf_counter() - t0
-        nb += 1
+    # decode: the first `nb` batch entries, sized the same way
+    t0 = time.perf_counter()
+    q1, k1, v1 = (np.ascontiguousarray(x[:1], dtype=np.float64) for x in (q4, k4, v4))
+    oracle.attention(q1, k1, v1, False, w4.scale)
+    nb = max(1, min(w4.B, int(budget_s / max(time.perf_counter() - t0, 1e-6))))
+    del q1, k1, v1
+    q64, k64, v64 = (np.ascontiguousarray(x[:nb], dtype=np.float64) for x in (q4, k4, v4))
+    t_dec, runs_dec = median_time(lambda: oracle.attention(q64, k64, v64, False, w4.scale))
+    del q64, k64, v64
     dec_gbps = 2.0 * nb * w4.H * w4.Sk * w4.D * 2 / t_dec / 1e9
     return {
         "value": round(pre_tflops, 6),
         "unit": "TFLOPS",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"prefill: {heads} of {w3.H} heads of the causal (1,32,4096,4096,128) workload "
-                  f"({t_pre:.1f} s); decode: {nb} of {w4.B} batch entries of (16,32,1,8192,128) "
-                  f"({t_dec:.1f} s), fp64 numpy",
+        "sample": f"prefill: {heads} of {w3.H} heads of the causal (1,32,4096,4096,128) workload, "
+                  f"{t_pre:.2f} s (median of {runs_pre}); decode: {nb} of {w4.B} batch entries of "
+                  f"(16,32,1,8192,128), {t_dec:.2f} s (median of {runs_dec}); fp64 numpy, inputs widened "
+                  "to fp64 before the timer",
         "decode_value": round(dec_gbps, 4),
         "decode_unit": "GB/s",
+        "cpu_model": cpu_model(),
+        "affinity_cores": AFFINITY_CORES,
+        "blas_threads": blas_threads(),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
     }
 
 
@@ -319,6 +363,26 @@ def main():
         f"decode {t_dec * 1e6:.1f} us = {gbps:.1f} GB/s (ns={ns})")
     t_pre_hot = time_launches(torch, prefill, args.steps)
     log(f"prefill back-to-back (K/V cache-warm): {t_pre_hot * 1e6:.1f} us = {flops / t_pre_hot / 1e12:.1f} TFLOPS")
+
+    # The same decode in its two-kernel form: the smallest power-of-two split
+    # count that gives every CU 8 phase-one workgroups of 256 threads (the
+    # partitions that fill the CUs), then the log-sum-exp merge kernel; with
+    # a caller workspace, so the call allocates nothing.  Timed back to back.
+    ns2 = 1
+    while w4.B * w4.H * ns2 < 8 * cus:
+        ns2 *= 2
+    ws2 = torch.empty(fa.fa_decode_workspace_bytes(w4.B, w4.H, w4.D, ns2), dtype=torch.uint8, device=dev)
+    o4b, l4b = torch.empty_like(o4), torch.empty_like(l4)
+
+    def decode_two_kernel():
+        fa.fa_decode_splitkv_ws(q4, k4, v4, ws2, o4b, l4b, scale=w4.scale, num_splits=ns2)
+
+    for _ in range(args.warmup):
+        decode_two_kernel()
+    t_dec2 = time_launches(torch, decode_two_kernel, args.steps)
+    gbps2 = kv_bytes / t_dec2 / 1e9
+    log(f"decode two-kernel form (ns={ns2}, caller workspace): {t_dec2 * 1e6:.1f} us = {gbps2:.1f} GB/s")
+    del ws2, o4b, l4b
 
     # Paged decoding of the same K / V, held in 16-token pages in a seeded
     # random physical order (built on the GPU, untimed); timed back to back.
@@ -497,7 +561,7 @@ def main():
 
     # Context, not the metric: what a plain 16-byte non-temporal read stream
     # (over the 1 GiB K cache) and a plain register-only fp16 MFMA loop reach
-    # on this GPU right now (tests/hip/roofline_probe.hip).
+    # on this GPU right now (exact_attention_54_amd/csrc/roofline_probe.hip).
     context = roofline_context(torch, dev, k4, cus, args.warmup)
     log(f"context: plain HBM read stream {context['context_stream_read_gbps']:.1f} GB/s; "
         f"plain fp16 MFMA loop {context['context_mfma_loop_tflops']:.1f} TFLOPS")
@@ -549,6 +613,10 @@ def main():
             "prefill_us": round(t_pre * 1e6, 2),
             "decode_us": round(t_dec * 1e6, 2),
             "prefill_us_back_to_back": round(t_pre_hot * 1e6, 2),
+            "decode_two_kernel_splits": ns2,
+            "decode_two_kernel_us": round(t_dec2 * 1e6, 2),
+            "decode_two_kernel_gbps": round(gbps2, 2),
+            "decode_two_kernel_frac_of_peak": round(gbps2 / PEAK_HBM_GBPS, 4),
             "paged_decode_gbps": round(gbps_paged, 2),
             "paged_decode_frac_of_peak": round(gbps_paged / PEAK_HBM_GBPS, 4),
             "paged_decode_us": round(t_paged * 1e6, 2),

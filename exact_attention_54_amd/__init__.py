@@ -6,6 +6,7 @@ the HIP kernels do all of the work.  There is no fallback path: if the
 library is missing or the tensors are not on a GPU, the call raises.
 
     o, lse = fa_fwd(q, k, v, causal=True)                  # q,k,v fp16 [B,H,S,D]
+    o, lse = fa_fwd_ws(q, k, v, workspace, causal=True)    # caller-owned workspace
     o, lse = fa_decode_splitkv(q, k, v, num_splits=0)      # Sq == 1, 0 = auto
     o, lse = fa_decode_paged(q, k_cache, v_cache, block_tables, seq_lens)
     o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)  # packed [total, H, D]
@@ -20,6 +21,8 @@ from ._capi import FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_OK, FA
 
 __all__ = [
     "fa_fwd",
+    "fa_fwd_ws",
+    "fa_fwd_workspace_bytes",
     "fa_fwd_varlen",
     "fa_bwd",
     "fa_decode_splitkv",
@@ -81,12 +84,6 @@ def _outputs(q, o, lse):
 def _stream(q, stream):
     torch = _torch()
     if stream is None:
-        # the current stream's handle without building a Stream object
-        # (~0.1 us against ~2 us, which dominated the host cost of a call)
-        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-        if raw is not None:
-            idx = q.device.index
-            return raw(torch.cuda.current_device() if idx is None else idx)
         stream = torch.cuda.current_stream(q.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -102,6 +99,30 @@ def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None):
                     B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream))
     _capi.check(st, "fa_fwd")
     return o, lse
+
+
+def fa_fwd_ws(q, k, v, workspace, o=None, lse=None, causal=False, scale=None, stream=None):
+    """fa_fwd with a caller-owned workspace tensor (any dtype, contiguous, on q's device; None when
+    fa_fwd_workspace_bytes is 0).  Nothing is allocated.  See fa_fwd_ws in include/fa.h."""
+    B, H, Sq, Sk, D = _check_qkv(q, k, v)
+    o, lse = _outputs(q, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ptr, nbytes = 0, 0
+    if workspace is not None:
+        if not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be contiguous and on q's device")
+        ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    lib = _capi.load()
+    st = lib.fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, Sq, Sk, D, int(bool(causal)), float(scale), _stream(q, stream), ptr or None, nbytes)
+    _capi.check(st, "fa_fwd_ws")
+    return o, lse
+
+
+def fa_fwd_workspace_bytes(B, H, Sq, Sk, D, causal, num_cus):
+    """Workspace bytes fa_fwd / fa_fwd_ws use for these sizes on num_cus CUs (0: none)."""
+    return int(_capi.load().fa_fwd_workspace_bytes(B, H, Sq, Sk, D, int(bool(causal)), num_cus))
 
 
 def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, causal=False, scale=None, stream=None):

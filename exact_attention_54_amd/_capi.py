@@ -24,6 +24,8 @@ _S = ctypes.c_size_t
 _COMMON = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]
 SIGNATURES = {
     "fa_fwd": (_I, _COMMON),
+    "fa_fwd_ws": (_I, _COMMON + [_P, _S]),
+    "fa_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_decode_splitkv": (_I, _COMMON + [_I]),

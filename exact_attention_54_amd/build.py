@@ -3,10 +3,11 @@
     python -m exact_attention_54_amd.build        # or __graft_entry__.build()
 
 Produces ``exact_attention_54_amd/libfa_hip.so`` from ``csrc/fa_api.hip``
-(the C ABI of ``include/fa.h`` plus every kernel), the test-only MFMA
-layout probe ``tests/hip/libmfma_probe.so`` and the streaming-read / MFMA
-loop probes ``tests/hip/libroofline_probe.so`` that bench.py reports as
-context.  Always recompiles.
+(the C ABI of ``include/fa.h`` plus every kernel), the streaming-read /
+MFMA loop probes ``exact_attention_54_amd/libroofline_probe.so`` from
+``csrc/roofline_probe.hip`` that bench.py reports as context, and the
+test-only MFMA layout probe ``tests/hip/libmfma_probe.so``.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -81,8 +82,8 @@ def build_test_probe(verbose: bool = False) -> str:
     return compile_shared([PROBE_SRC], PROBE_LIB, verbose=verbose)
 
 
-ROOFLINE_SRC = os.path.join(ROOT, "tests", "hip", "roofline_probe.hip")
-ROOFLINE_LIB = os.path.join(ROOT, "tests", "hip", "libroofline_probe.so")
+ROOFLINE_SRC = os.path.join(CSRC, "roofline_probe.hip")
+ROOFLINE_LIB = os.path.join(PKG, "libroofline_probe.so")
 
 
 def build_roofline_probe(verbose: bool = False) -> str:

@@ -80,28 +80,6 @@ int device_cu_count(int* out);
 int workspace_pool(hipMemPool_t* out);
 size_t ws_bytes(int64_t BH, int D, int ns);
 
-// Workspace of the key-split forward passes (partial O and LSE), one per
-// device, kept for the life of the process and grown when a call needs
-// more.  A call holds it from acquire to the end of its launches; every call
-// records an event on its stream after them, and a call on another stream
-// first makes its stream wait for that event, so calls on different streams
-// take turns on the GPU instead of racing.  Steady state: no allocation,
-// one event record per call.
-class FwdWorkspace {
- public:
-  FwdWorkspace() = default;
-  FwdWorkspace(const FwdWorkspace&) = delete;
-  FwdWorkspace& operator=(const FwdWorkspace&) = delete;
-  ~FwdWorkspace();
-  // buffer of at least `bytes` bytes usable by work queued on `s` from now on
-  int acquire(size_t bytes, hipStream_t s, void** out);
-
- private:
-  std::unique_lock<std::mutex> lock_;
-  int dev_ = -1;
-  hipStream_t stream_ = nullptr;
-};
-
 // Key-range split of a small prefill grid (fa::KeySplit): which query tiles
 // to split (ts .. nqt-1) and into how many parts, chosen by simulating the
 // dispatch.  Times are in units of one key tile of one query tile.
@@ -169,17 +147,6 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
   SplitPlan best;
   const SplitModel m = fwd_split_model(D);
   if (cus < 1 || (int64_t)nqt * BH > 2 * (int64_t)cus || (m.causal_only && !causal)) return best;
-  static std::mutex mu;
-  struct Entry {
-    int key[8];
-    SplitPlan plan;
-  };
-  static Entry cache[16];
-  static int next = 0;
-  const int key[8] = {nqt, BH, BM, BN, D, Sq, Sk, (causal ? 1 : 0) | (cus << 1)};
-  std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& e : cache)
-    if (std::equal(key, key + 8, e.key)) return e.plan;
   double best_cost = m.min_gain * fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, cus, m);
   const int starts[4] = {0, nqt / 4, nqt / 2, 3 * nqt / 4};
   const int parts[5] = {2, 3, 4, 6, 8};
@@ -201,25 +168,16 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
       }
     }
   }
-  Entry& e = cache[next];
-  next = (next + 1) % 16;
-  std::copy(key, key + 8, e.key);
-  e.plan = best;
   return best;
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-                     float scale, hipStream_t stream, const SplitPlan& pl) {
+                     float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
   using Cfg = fa::FwdCfg<D, BN, NW>;
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   const int nsplit = nqt - pl.ts;
   const int64_t rows = (int64_t)BH * nsplit * Cfg::BM;
-  if (rows > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  FwdWorkspace wsp;
-  void* ws = nullptr;
-  int rc = wsp.acquire(ws_bytes(rows, D, pl.ns), stream, &ws);
-  if (rc != FA_OK) return rc;
   fa::KeySplit ksp;
   ksp.ts = pl.ts;
   ksp.ns = pl.ns;
@@ -229,7 +187,7 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
                      dim3(Cfg::THREADS), 0, stream, static_cast<const _Float16*>(q),
                      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o),
                      lse, Sq, Sk, BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
-  rc = launched("fa_fwd key-split kernel launch");
+  int rc = launched("fa_fwd key-split kernel launch");
   if (rc == FA_OK) {
     constexpr int R = fa::MergeCfg<D>::ROWS;
     hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
@@ -242,43 +200,31 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
 
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-               float scale, hipStream_t stream) {
+               float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
   using Cfg = fa::FwdCfg<D, BN, NW>;
+  if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  const float c2 = scale * fa::kLog2e;
-  if constexpr (D == 256 || NW == 4) {
-    // small grids: the heaviest (causal) tiles, or too few tiles, leave CUs idle
-    int cus = 0;
-    int rc = device_cu_count(&cus);
-    if (rc != FA_OK) return rc;
-    const SplitPlan pl = plan_fwd_split(nqt, BH, Cfg::BM, BN, D, Sq, Sk, CAUSAL, cus);
-    if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl);
-  }
   hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
                      static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt, c2);
+                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt,
+                     scale * fa::kLog2e);
   return launched("fa_fwd kernel launch");
 }
 
-// D <= 128: 8-wavefront workgroups (256 query rows, one per CU) when that
-// still gives every CU a workgroup, else 4-wavefront ones (128 rows, two per
-// CU) so small problems spread over more CUs.
+// The tile kernel of head dim D with the geometry the plan chose: D = 256
+// 32-key tiles; D = 32 always 128-row workgroups (a 64-key tile of D = 32
+// is 4 KiB: one 1 KiB copy for each of 4 wavefronts); D = 64, 128 256-row
+// workgroups when the plan says so.
 template <int D, bool CAUSAL>
 int launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-                 float scale, hipStream_t stream) {
+                 float scale, hipStream_t stream, int nw, const SplitPlan& pl, void* ws) {
   if constexpr (D == 256) {
-    return launch_fwd<256, 32, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    return launch_fwd<256, 32, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   } else if constexpr (D == 32) {
-    // a 64-key tile of D = 32 is 4 KiB: one 1 KiB copy for each of 4 wavefronts
-    return launch_fwd<32, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    return launch_fwd<32, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   } else {
-    int cus = 0;
-    int rc = device_cu_count(&cus);
-    if (rc != FA_OK) return rc;
-    const int64_t wg8 = (int64_t)BH * ((Sq + 255) / 256);
-    if (wg8 >= cus) return launch_fwd<D, 64, 8, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
-    return launch_fwd<D, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    if (nw == 8) return launch_fwd<D, 64, 8, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
+    return launch_fwd<D, 64, 4, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   }
 }
 
@@ -485,62 +431,6 @@ int workspace_pool(hipMemPool_t* out) {
   return FA_OK;
 }
 
-struct FwdWsSlot {
-  std::mutex mu;
-  void* buf = nullptr;
-  size_t bytes = 0;
-  hipEvent_t done = nullptr;  // recorded after the last call's launches
-  hipStream_t stream = nullptr;
-  bool used = false;
-};
-FwdWsSlot g_fwd_ws[kMaxDevices];
-
-int FwdWorkspace::acquire(size_t bytes, hipStream_t s, void** out) {
-  int dev = 0;
-  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
-  if (rc != FA_OK) return rc;
-  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
-  FwdWsSlot& w = g_fwd_ws[dev];
-  lock_ = std::unique_lock<std::mutex>(w.mu);
-  if (!w.done) {
-    rc = hip_check(hipEventCreateWithFlags(&w.done, hipEventDisableTiming), "workspace event");
-    if (rc != FA_OK) return rc;
-  }
-  if (w.bytes < bytes) {
-    // growth (rare): wait until the last call's kernels are done with the old buffer
-    if (w.used) {
-      rc = hip_check(hipEventSynchronize(w.done), "workspace event wait");
-      if (rc != FA_OK) return rc;
-    }
-    if (w.buf) (void)hipFree(w.buf);
-    w.buf = nullptr;
-    w.bytes = 0;
-    rc = hip_check(hipMalloc(&w.buf, bytes), "workspace allocation");
-    if (rc != FA_OK) return rc;
-    w.bytes = bytes;
-  } else if (w.used && w.stream != s) {
-    rc = hip_check(hipStreamWaitEvent(s, w.done, 0), "workspace stream wait");
-    if (rc != FA_OK) return rc;
-  }
-  dev_ = dev;
-  stream_ = s;
-  *out = w.buf;
-  return FA_OK;
-}
-
-FwdWorkspace::~FwdWorkspace() {
-  if (dev_ < 0) return;
-  FwdWsSlot& w = g_fwd_ws[dev_];
-  if (hipEventRecord(w.done, stream_) == hipSuccess) {
-    w.used = true;
-    w.stream = stream_;
-  } else {
-    // no event to order the next call after this one: wait here instead
-    (void)hipStreamSynchronize(stream_);
-    w.used = false;
-  }
-}
-
 size_t ws_bytes(int64_t BH, int D, int ns) {
   const size_t floats = (size_t)BH * ns * (D + 1);
   return (floats * 4 + 255) / 256 * 256;
@@ -561,23 +451,9 @@ int splitd_parts(int64_t work_items, int nkt_all, int cus) {
 
 template <int D>
 int run_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-                   int causal, float scale, hipStream_t s) {
-  const int nqt = (Sq + 31) / 32;
-  if ((int64_t)nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  int cus = 0;
-  int rc = device_cu_count(&cus);
-  if (rc != FA_OK) return rc;
-  const int ns = splitd_parts((int64_t)nqt * BH, (Sk + 31) / 32, cus);
-  float* ws_o = nullptr;
-  float* ws_lse = nullptr;
-  FwdWorkspace wsp;
-  if (ns > 1) {
-    void* ws = nullptr;
-    rc = wsp.acquire(ws_bytes((int64_t)BH * Sq, D, ns), s, &ws);
-    if (rc != FA_OK) return rc;
-    ws_o = static_cast<float*>(ws);
-    ws_lse = ws_o + (size_t)BH * Sq * ns * D;
-  }
+                   int causal, float scale, hipStream_t s, int ns, void* ws) {
+  float* ws_o = static_cast<float*>(ws);  // unused (may be null) without a key split
+  float* ws_lse = ns > 1 ? ws_o + (size_t)BH * Sq * ns * D : nullptr;
   return causal ? launch_fwd_splitd<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse)
                 : launch_fwd_splitd<D, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse);
 }
@@ -674,6 +550,93 @@ int resolve_splits(int B, int H, int Sk, int num_splits, int* ns) {
   return FA_OK;
 }
 
+// How fa_fwd runs a call of these sizes on a device with `cus` CUs: the
+// kernel, its geometry, its key split and the workspace bytes it needs.  A
+// pure function of its arguments, so fa_fwd, fa_fwd_ws and the two query
+// functions always agree.
+enum FwdKind { kFwdTile = 0, kFwdSplitD = 1, kFwdDecode = 2 };
+struct FwdPlan {
+  int kind = kFwdTile;
+  int nw = 4;     // wavefronts per workgroup of the tile kernel
+  SplitPlan sp;   // key split of the tile kernel (sp.ns > 1: split)
+  int ns = 1;     // key parts of Split-D, or decode partitions
+  size_t ws = 0;  // workspace bytes (0: none)
+};
+
+int plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, FwdPlan* out) {
+  FwdPlan p;
+  const int64_t BH = (int64_t)B * H;
+  if (BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  if (Sq == 1 && !causal && D <= 256) {
+    // a single query row attending to every key is a decode step: the
+    // split-KV path ("FlashAttention-2 MMA", Architecture & Dispatch Flow,
+    // seq_q == 1).  Causal single rows see key 0 only (top-left mask) and
+    // stay on the tile kernel.
+    p.kind = kFwdDecode;
+    p.ns = fa_decode_auto_splits(B, H, Sk, cus);
+    if (p.ns < 1) return fail(FA_ERR_INVALID_ARG, "could not choose a split count");
+    if (BH * p.ns > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    p.ws = p.ns > 1 ? ws_bytes(BH, D, p.ns) : 0;
+  } else if (D >= 512) {
+    p.kind = kFwdSplitD;
+    const int64_t nqt = (Sq + 31) / 32;
+    if (nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    p.ns = splitd_parts(nqt * BH, (Sk + 31) / 32, cus);
+    p.ws = p.ns > 1 ? ws_bytes(BH * Sq, D, p.ns) : 0;
+  } else {
+    int BM = 128, BN = 64;
+    if (D == 256) {
+      BN = 32;
+    } else if (D != 32 && BH * ((Sq + 255) / 256) >= cus) {
+      // D = 64, 128: 256-row workgroups (one per CU) when that still gives
+      // every CU one, else 128-row ones (two per CU) so small problems
+      // spread over more CUs
+      p.nw = 8;
+      BM = 256;
+    }
+    const int64_t nqt = (Sq + BM - 1) / BM;
+    if (nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    // small grids: the heaviest causal tiles, or too few tiles, leave CUs idle
+    if (p.nw == 4) p.sp = plan_fwd_split((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus);
+    if (p.sp.ns > 1) p.ws = ws_bytes(BH * (nqt - p.sp.ts) * BM, D, p.sp.ns);
+  }
+  *out = p;
+  return FA_OK;
+}
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk, int D,
+            int causal, float scale, hipStream_t s, const FwdPlan& p, void* ws) {
+  const int BH = B * H;
+  if (p.kind == kFwdDecode) return run_decode(q, k, v, o, lse, BH, Sk, D, scale, s, p.ns, ws);
+  switch (D) {
+    case 32:
+      return causal ? launch_fwd_d<32, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws)
+                    : launch_fwd_d<32, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws);
+    case 64:
+      return causal ? launch_fwd_d<64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws)
+                    : launch_fwd_d<64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws);
+    case 128:
+      return causal ? launch_fwd_d<128, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws)
+                    : launch_fwd_d<128, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws);
+    case 256:
+      return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws)
+                    : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws);
+    case 512:
+      return run_fwd_splitd<512>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws);
+    default:
+      return run_fwd_splitd<1024>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws);
+  }
+}
+
+// A workspace of `bytes` from the device's stream-ordered pool, usable by
+// work queued on `s` from now on; release with hipFreeAsync on `s`.
+int pool_alloc(size_t bytes, hipStream_t s, void** out) {
+  hipMemPool_t pool = nullptr;
+  int rc = workspace_pool(&pool);
+  if (rc != FA_OK) return rc;
+  return hip_check(hipMallocFromPoolAsync(out, bytes, pool, s), "workspace allocation");
+}
+
 }  // namespace
 
 extern "C" {
@@ -682,32 +645,45 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int causal, float scale, void* stream) {
   int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
   if (rc != FA_OK) return rc;
-  // a single query row attending to every key is a decode step: the split-KV
-  // path ("FlashAttention-2 MMA", Architecture & Dispatch Flow, seq_q == 1).
-  // Causal single rows see key 0 only (top-left mask) and stay on Split-Q.
-  if (Sq == 1 && causal == 0 && D <= 256)
-    return fa_decode_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, 0, scale, stream, 0);
-  const int BH = B * H;
-  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  int cus = 0;
+  rc = device_cu_count(&cus);
+  if (rc != FA_OK) return rc;
+  FwdPlan p;
+  rc = plan_fwd(B, H, Sq, Sk, D, causal != 0, cus, &p);
+  if (rc != FA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (D) {
-    case 32:
-      return causal ? launch_fwd_d<32, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_d<32, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
-    case 64:
-      return causal ? launch_fwd_d<64, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_d<64, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
-    case 128:
-      return causal ? launch_fwd_d<128, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_d<128, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
-    case 256:
-      return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s)
-                    : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s);
-    case 512:
-      return run_fwd_splitd<512>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s);
-    default:
-      return run_fwd_splitd<1024>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s);
-  }
+  if (p.ws == 0) return run_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, s, p, nullptr);
+  void* ws = nullptr;
+  rc = pool_alloc(p.ws, s, &ws);
+  if (rc != FA_OK) return rc;
+  rc = run_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, s, p, ws);
+  const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
+  return rc != FA_OK ? rc : frc;
+}
+
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk, int D,
+              int causal, float scale, void* stream, void* workspace, size_t workspace_bytes) {
+  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  if (workspace && !aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int cus = 0;
+  rc = device_cu_count(&cus);
+  if (rc != FA_OK) return rc;
+  FwdPlan p;
+  rc = plan_fwd(B, H, Sq, Sk, D, causal != 0, cus, &p);
+  if (rc != FA_OK) return rc;
+  if (p.ws > 0 && (!workspace || workspace_bytes < p.ws))
+    return fail(FA_ERR_INVALID_ARG, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : 0, p.ws);
+  return run_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, static_cast<hipStream_t>(stream), p,
+                 p.ws ? workspace : nullptr);
+}
+
+size_t fa_fwd_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal, int num_cus) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || num_cus < 1 || (causal != 0 && causal != 1)) return 0;
+  if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return 0;
+  FwdPlan p;
+  if (plan_fwd(B, H, Sq, Sk, D, causal != 0, num_cus, &p) != FA_OK) return 0;
+  return p.ws;
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
@@ -742,7 +718,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
-  if (D > 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
   if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;
@@ -766,31 +742,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
 int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus) {
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || num_cus < 1 || (causal != 0 && causal != 1)) return 0;
-  if ((int64_t)B * H > kMaxGrid) return 0;
-  const int BH = B * H;
-  switch (D) {
-    case 32:
-    case 64:
-    case 128: {
-      // the 8-wavefront kernel (grids that give every CU a workgroup) is never split
-      if (D != 32 && (int64_t)BH * ((Sq + 255) / 256) >= num_cus) return 1;
-      using Cfg = fa::FwdCfg<128, 64, 4>;
-      const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-      return plan_fwd_split(nqt, BH, Cfg::BM, 64, D, Sq, Sk, causal != 0, num_cus).ns;
-    }
-    case 256: {
-      using Cfg = fa::FwdCfg<256, 32, 4>;
-      const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-      return plan_fwd_split(nqt, BH, Cfg::BM, 32, 256, Sq, Sk, causal != 0, num_cus).ns;
-    }
-    case 512:
-    case 1024: {
-      const int64_t nqt = (Sq + 31) / 32;
-      return splitd_parts(nqt * BH, (Sk + 31) / 32, num_cus);
-    }
-    default:
-      return 0;
-  }
+  if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return 0;
+  FwdPlan p;
+  if (plan_fwd(B, H, Sq, Sk, D, causal != 0, num_cus, &p) != FA_OK) return 0;
+  return p.kind == kFwdTile ? p.sp.ns : p.ns;
 }
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {

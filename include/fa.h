@@ -33,9 +33,7 @@
  *   Stream    `stream` is a hipStream_t passed as void* (NULL = the null
  *             stream).  Every call only enqueues work on that stream and
  *             returns; results are valid once the stream has reached them.
- *             (One exception: a key-split fa_fwd call that needs a larger
- *             forward workspace first waits, on the host, for the previous
- *             key-split call's kernels; see fa_fwd.)
+ *             No call waits on the host or makes one stream wait for another.
  *   Causal    top-left aligned: query row i sees keys 0..i (all keys when
  *             i >= Sk), so no row is ever fully masked.
  *   Scale     any finite scale > 0 (the pages use 1/sqrt(D)).
@@ -47,11 +45,11 @@
  *             validated on the host before any HIP call, so an invalid call
  *             enqueues nothing.  FA_ERR_HIP reports a failed HIP launch or
  *             allocation; fa_last_error() then names it.
- *   Threads   calls hold no global mutable state apart from a per-device CU
- *             count cache, a per-device workspace memory pool (created under
- *             a lock), a per-device forward workspace (used under a lock, see
- *             fa_fwd), a small cache of fa_fwd split plans and a thread-local
- *             error message; they may be made from several threads at once.
+ *   Threads   the library's only state is a per-device CU count cache, a
+ *             per-device stream-ordered workspace memory pool (created once,
+ *             under a lock) and a thread-local error message; calls share no
+ *             buffer with each other and may be made from several threads
+ *             and on several streams at once.
  */
 #ifndef FA_H
 #define FA_H
@@ -92,11 +90,11 @@ enum fa_status {
  * whose heaviest query tiles would leave most CUs idle near the end has the
  * key ranges of those tiles split, when fa_fwd_key_splits() says it pays; a
  * second kernel merges the parts.  Split calls keep their fp32 partials in
- * a per-device workspace that the library allocates on first need, grows
- * when a call needs more (after the previous call's kernels are done with
- * it) and keeps until the process ends; a call on another stream than the
- * previous split call first waits on the GPU for that call's kernels, so
- * split calls on one device run one after another.
+ * a workspace of fa_fwd_workspace_bytes() bytes taken from the per-device
+ * stream-ordered pool (hipMallocFromPoolAsync before the kernels,
+ * hipFreeAsync after them, both on `stream`), so nothing blocks and calls on
+ * different streams never share a buffer; fa_fwd_ws is the same call with a
+ * caller-owned workspace.
  * Any Sq works.  A non-causal call with Sq = 1 and D <= 256 is a decode step
  * and runs fa_decode_splitkv with the automatic split count (the page's
  * dispatch of seq_q == 1 to Split-KV); with causal = 1 a single row sees
@@ -106,6 +104,31 @@ enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Sq, int Sk, int D, int causal, float scale,
            void* stream);
+
+/*
+ * fa_fwd_workspace_bytes -- bytes of device workspace that fa_fwd (from its
+ * pool) and fa_fwd_ws (from the caller) use for these sizes on a device with
+ * num_cus CUs: 0 when the call runs without one (no key split, and a decode
+ * step with one partition); otherwise the fp32 partial outputs and LSEs of
+ * the key parts, rows * parts * (D + 1) * 4 bytes rounded up to 256, where
+ * rows are the query rows of the split tiles (B * H * Sq for Split-D, and
+ * B * H for a decode step).  Pure host arithmetic; returns 0 for invalid
+ * sizes too.
+ */
+size_t fa_fwd_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
+
+/*
+ * fa_fwd_ws -- fa_fwd with a caller-provided device workspace: at least
+ * fa_fwd_workspace_bytes(B, H, Sq, Sk, D, causal, CUs of the current device)
+ * bytes, 16-byte aligned; it may be NULL when that is 0.  Nothing is
+ * allocated.  Same computation, kernels, stream behaviour and results as
+ * fa_fwd.  A smaller workspace returns FA_ERR_INVALID_ARG before any launch.
+ * Calls that share one workspace must be ordered on one stream (or
+ * otherwise serialised by the caller); the workspace holds no result.
+ */
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Sq, int Sk, int D, int causal, float scale,
+              void* stream, void* workspace, size_t workspace_bytes);
 
 /*
  * fa_bwd -- gradients of exact attention from the forward's outputs
@@ -259,8 +282,9 @@ int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
  * CU that frees first) against the cost of merging the parts, with timing
  * constants measured per kernel; at most 8 parts.  Other D = 64, 128 grids:
  * 1.  D = 512, 1024: the Split-D key split (enough parts to give every CU a
- * work item when there are fewer than CUs, at most 16).  Pure host
- * arithmetic; returns 0 for invalid sizes.
+ * work item when there are fewer than CUs, at most 16).  A decode step
+ * (Sq = 1, causal = 0, D <= 256): the partitions of fa_decode_auto_splits.
+ * Pure host arithmetic; returns 0 for invalid sizes.
  */
 int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
 

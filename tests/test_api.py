@@ -196,12 +196,73 @@ def test_fwd_key_splits_properties_on_random_shapes(lib):
         cus = int(g.choice([80, 256, 304]))
         ns = lib.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus)
         assert 1 <= ns <= (16 if D >= 512 else 8), (B, H, Sq, Sk, D, causal, cus, ns)
+        if Sq == 1 and not causal and D <= 256:
+            # a decode step: the decode's partitions
+            assert ns == lib.fa_decode_auto_splits(B, H, Sk, cus), (B, H, Sk, D, cus, ns)
+            continue
         if D in (64, 128) and (not causal or B * H * -(-Sq // 256) >= cus):
             assert ns == 1, (B, H, Sq, Sk, D, causal, cus, ns)
         if D <= 256 and B * H * -(-Sq // 128) > 2 * cus:
             assert ns == 1, (B, H, Sq, Sk, D, causal, cus, ns)
     assert lib.fa_fwd_key_splits(1, 1, 0, 5, 128, 1, 256) == 0
     assert lib.fa_fwd_key_splits(1, 1, 5, 5, 48, 1, 256) == 0
+
+
+def rup256(n):
+    return -(-n // 256) * 256
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,causal,cus", [
+    (1, 32, 4096, 4096, 128, 1, 256),
+    (1, 4, 4096, 4096, 128, 1, 256),
+    (1, 2, 8192, 8192, 128, 1, 256),
+    (1, 16, 1024, 1024, 256, 1, 256),
+    (1, 4, 2048, 2048, 256, 0, 256),
+    (1, 16, 2048, 2048, 256, 1, 256),
+    (1, 4, 512, 512, 1024, 0, 256),
+    (1, 8, 1024, 1024, 512, 1, 256),
+    (1, 8, 1, 32768, 128, 0, 256),     # a decode step with many partitions
+    (16, 32, 1, 8192, 128, 0, 256),    # a decode step with one partition
+    (1, 1, 1, 9, 64, 1, 256),          # causal single row: the tile kernel
+])
+def test_fwd_workspace_bytes(lib, B, H, Sq, Sk, D, causal, cus):
+    # the workspace follows the split choice: none without a split; otherwise
+    # the fp32 partial rows (D values and one LSE per part) of the split tiles
+    ns = lib.fa_fwd_key_splits(B, H, Sq, Sk, D, causal, cus)
+    ws = lib.fa_fwd_workspace_bytes(B, H, Sq, Sk, D, causal, cus)
+    if ns == 1:
+        assert ws == 0
+    elif Sq == 1 and not causal:
+        assert ws == lib.fa_decode_workspace_bytes(B, H, D, ns) == rup256(B * H * ns * (D + 1) * 4)
+    elif D >= 512:
+        assert ws == rup256(B * H * Sq * ns * (D + 1) * 4)
+    else:
+        # rows of the split 128-row query tiles: a whole number of tiles per slice
+        assert ws % 256 == 0 and ws > 0
+        tiles = -(-Sq // 128)
+        per_tile = 128 * ns * (D + 1) * 4
+        assert any(ws == rup256(B * H * t * per_tile) for t in range(1, tiles + 1)), ws
+
+
+def test_fwd_workspace_bytes_invalid(lib):
+    assert lib.fa_fwd_workspace_bytes(0, 1, 16, 16, 128, 0, 256) == 0
+    assert lib.fa_fwd_workspace_bytes(1, 1, 16, 16, 96, 0, 256) == 0
+    assert lib.fa_fwd_workspace_bytes(1, 1, 16, 16, 128, 2, 256) == 0
+    assert lib.fa_fwd_workspace_bytes(1, 1, 16, 16, 128, 0, 0) == 0
+
+
+def test_fwd_ws_rejects_before_any_hip_call(lib):
+    a = GOOD
+
+    def call(ws, nbytes=1 << 20, **kw):
+        b = dict(a, **kw)
+        return lib.fa_fwd_ws(P[0], P[1], P[2], P[3], P[4], b["B"], b["H"], b["Sq"], b["Sk"], b["D"], b["causal"],
+                             b["scale"], None, ws, nbytes)
+
+    assert call(A + 0x8008) == _capi.FA_ERR_INVALID_ARG    # misaligned workspace
+    assert "workspace" in _capi.last_error()
+    assert call(A + 0x8000, D=96) == _capi.FA_ERR_UNSUPPORTED
+    assert call(A + 0x8000, scale=0.0) == _capi.FA_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):
@@ -301,6 +362,20 @@ def test_paged_rejects_null_and_misaligned(lib, idx):
     ptrs = list(P[:3]) + list(TBL) + list(P[3:])
     ptrs[idx] += 2
     assert paged(lib, p=ptrs[:3] + ptrs[5:], t=ptrs[3:5]) == _capi.FA_ERR_INVALID_ARG
+
+
+def bwd(lib, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_bwd(P[0], P[1], P[2], P[3], P[4], A + 0x5000, A + 0x6000, A + 0x7000, A + 0x8000, a["B"], a["H"],
+                      a["Sq"], a["Sk"], a["D"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("D", [16, 32, 48, 96, 256, 512, 1024])
+def test_bwd_rejects_head_dims_without_a_kernel(lib, D):
+    # every head dim the backward has no kernel for is refused before any HIP
+    # call (the fake pointers are never touched)
+    assert bwd(lib, D=D) == _capi.FA_ERR_UNSUPPORTED
+    assert "head dim" in _capi.last_error()
 
 
 @pytest.mark.parametrize("D", [512, 1024])

@@ -68,7 +68,8 @@ def test_permlane32_swap_exchanges_wave_halves():
     assert hi.cpu().tolist() == xs[32:] + xs[32:]
 
 
-ROOFLINE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libroofline_probe.so")
+ROOFLINE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "exact_attention_54_amd",
+                        "libroofline_probe.so")
 
 
 def test_roofline_probes_run():

@@ -2,9 +2,10 @@
 
 Bar (fp16 unit-normal inputs): max |O - O_oracle| <= 2e-3 and
 max |LSE - LSE_oracle| <= 1e-3, element by element on the same seeded inputs.
-Full-size workloads are compared on every element where the oracle is quick
-(tiny, small, D=256 prefill, the 8K decode) and on whole heads plus sampled
-rows for the LLaMA-7B-shaped prefill.
+Every full-size workload is compared on every element (tiny, small, the
+LLaMA-7B-shaped prefill, D=256 prefill, and the 8K decode in both its
+one-kernel and two-kernel forms); sampled rows of the LLaMA-7B-shaped
+prefill are a fast subset.
 """
 import math
 
@@ -94,19 +95,29 @@ def test_llama_prefill_sampled_rows(llama):
     assert_close(o[idx], lse[idx], O, L, "llama7b sampled rows")
 
 
-@pytest.mark.parametrize("h", [0, 31])
-def test_llama_prefill_whole_head(llama, h):
+def test_llama_prefill_every_element(llama):
+    # the whole output: all 32 heads of O and LSE against the oracle
     w, q, k, v, o, lse = llama
-    O, L = oracle.attention(q[:, h : h + 1], k[:, h : h + 1], v[:, h : h + 1], True, w.scale)
-    assert_close(o[:, h : h + 1], lse[:, h : h + 1], O, L, f"llama7b head {h}")
+    O, L = oracle.attention(q, k, v, True, w.scale)
+    assert_close(o, lse, O, L, "llama7b every element")
 
 
-def test_decode_workload_full(torch_dev, fa):
+@pytest.fixture(scope="module")
+def decode_8k():
     w = WORKLOADS["decode_8k"]
     q, k, v = workload_inputs(w)
-    o, lse = gpu_decode(torch_dev, fa, q, k, v, w.scale, 0)
     O, L = oracle.attention(q, k, v, False, w.scale)
-    assert_close(o, lse, O, L, "decode_8k auto splits")
+    return w, q, k, v, O, L
+
+
+# 0: the library's automatic choice (one partition, merged in LDS, at this
+# size); 4: the two-kernel form with the partitions that fill the CUs
+# (B*H*ns = 2048 phase-one workgroups = 8 per CU) and the merge kernel
+@pytest.mark.parametrize("ns", [0, 4])
+def test_decode_workload_full(torch_dev, fa, decode_8k, ns):
+    w, q, k, v, O, L = decode_8k
+    o, lse = gpu_decode(torch_dev, fa, q, k, v, w.scale, ns)
+    assert_close(o, lse, O, L, f"decode_8k ns={ns}")
 
 
 # -------------------------------------------------- ragged and edge shapes
@@ -295,9 +306,10 @@ def test_side_stream(torch_dev, fa):
 
 
 def test_split_decodes_on_two_streams_and_growth(torch_dev, fa):
-    # split decodes share one workspace per device: queued back to back on
-    # two streams (each waits on the GPU for the other's previous call), the
-    # second size larger than the first (the workspace grows in between)
+    # split decodes queued back to back on two streams with no host sync:
+    # each call takes its own workspace from the stream-ordered pool on its
+    # stream and frees it there, and the split counts (so the workspace
+    # sizes) grow from one round to the next
     torch, dev = torch_dev
     cases = [make_qkv(1, 4, 1, 3000, 128, seed=81), make_qkv(2, 6, 1, 9000, 64, seed=82)]
     dev_in = [to_dev(torch_dev, *c) for c in cases]

@@ -6,9 +6,10 @@ scheme of "Adaptive High-Performance Attention Kernels in CUDA", Split-K /
 Flash-Decoding, on prefill tiles).  Every shape here is checked to be one
 that fa_fwd_key_splits() splits on this device, so these tests run the
 split kernel and its merge; the bar is the one of every prefill: max |dO|
-<= 2e-3, max |dLSE| <= 1e-3.  Also covered: bitwise repeatability, the
-workspace growing between calls queued without a sync, and split calls on
-two streams taking turns on the shared workspace.
+<= 2e-3, max |dLSE| <= 1e-3.  Also covered: bitwise repeatability, split
+calls of different workspace sizes queued without a sync, split calls on two
+streams at once (each with its own pool workspace), and fa_fwd_ws with a
+caller workspace (bit-identical to fa_fwd; a short workspace is refused).
 """
 import math
 
@@ -57,10 +58,10 @@ def check(o, lse, O, L, what):
     assert el <= LSE_TOL, f"{what}: max|dLSE| = {el:.3e}"
 
 
-def test_workspace_grows_between_queued_calls(env):
+def test_split_calls_of_different_sizes_queued(env):
     # small split call, the largest split call of this file, small again,
-    # queued back to back: the second grows the workspace after the first's
-    # kernels are done with it
+    # queued back to back without a sync: each takes a workspace of its own
+    # size from the stream-ordered pool and returns it on the stream
     torch = env[0]
     small = inputs(env, 1, 2, 1000, 1000, True, seed=31)
     large = inputs(env, 1, 4, 2048, 2048, False, seed=32)
@@ -120,8 +121,9 @@ def test_split_run_to_run_bitwise(env):
 
 
 def test_split_calls_on_two_streams(env):
-    # split calls alternate between two streams with no host sync: each
-    # waits on the GPU for the previous call's use of the shared workspace
+    # split calls alternate between two streams with no host sync; each
+    # call's workspace comes from the pool on its own stream, so the two
+    # streams run concurrently without sharing a buffer
     torch, dev, fa, _ = env
     shapes = [(1, 2, 1000, 1000, True), (1, 3, 200, 333, False)]
     cases = [inputs(env, B, H, Sq, Sk, c, seed=60 + i) + (c,) for i, (B, H, Sq, Sk, c) in enumerate(shapes)]
@@ -176,3 +178,31 @@ def test_split_head_shard_of_llama_prefill_sampled_rows(env, d):
     O, L = oracle.attention_rows(*host, True, scale, rows)
     idx = tuple(np.array(rows).T)
     check(o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], O, L, f"head shard D={d} sampled rows ns={ns}")
+
+
+def test_fwd_ws_caller_workspace_matches_fwd(env):
+    # fa_fwd_ws with a caller workspace of exactly fa_fwd_workspace_bytes is
+    # bit-identical to fa_fwd (same plan, same kernels); one byte short is
+    # refused before any launch
+    torch, dev, fa, cus = env
+    host, dev_in, ns = inputs(env, 1, 16, 1024, 1024, True, seed=71)
+    nbytes = fa.fa_fwd_workspace_bytes(1, 16, 1024, 1024, D, True, cus)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a = fa.fa_fwd(*dev_in, causal=True, scale=1 / 16)
+    b = fa.fa_fwd_ws(*dev_in, ws, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    O, L = oracle.attention(*host, True, 1 / 16)
+    check(b[0], b[1], O, L, f"fa_fwd_ws ns={ns}")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd_ws(*dev_in, ws[:-1], causal=True, scale=1 / 16)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
+    # an unsplit call needs no workspace
+    q, k, v = make_qkv(1, 2, 300, 300, 64, seed=72)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    assert fa.fa_fwd_workspace_bytes(1, 2, 300, 300, 64, False, cus) == 0
+    o, lse = fa.fa_fwd_ws(qd, kd, vd, None, causal=False, scale=0.125)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, False, 0.125)
+    check(o, lse, O, L, "fa_fwd_ws without workspace")
