@@ -31,6 +31,7 @@ SIGNATURES = {
     "fa_decode_splitkv": (_I, _COMMON + [_I]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "fa_decode_splitkv_ws": (_I, _COMMON + [_I, _P, _S]),
+    "fa_decode_splitkv_noalloc": (_I, _COMMON + [_I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _I]),
     "fa_decode_auto_splits": (_I, [_I, _I, _I, _I]),
     "fa_fwd_key_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),

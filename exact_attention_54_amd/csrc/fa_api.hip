@@ -628,6 +628,36 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   }
 }
 
+// Static scratch of fa_decode_splitkv_noalloc: the phase-one partials of a
+// split decode, in a file-scope device array that every GPU the library
+// runs on holds (its own copy) until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a
+// stand-in symbol): the device address of each GPU's copy is looked up once
+// per device with hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`, resolved on the first call on
+// that device (with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != FA_OK) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (rc != FA_OK) return rc;
+    if (!p) return fail(FA_ERR_HIP, "scratch symbol address is null");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
 // A workspace of `bytes` from the device's stream-ordered pool, usable by
 // work queued on `s` from now on; release with hipFreeAsync on `s`.
 int pool_alloc(size_t bytes, hipStream_t s, void** out) {
@@ -801,6 +831,25 @@ int fa_decode_splitkv(const void* q, const void* k, const void* v, void* o, floa
   rc = run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, ns, ws);
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
+}
+
+int fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                              int Sk, int D, int causal, float scale, void* stream, int num_splits) {
+  int rc = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, num_splits);
+  if (rc != FA_OK) return rc;
+  int ns = 0;
+  rc = resolve_splits(B, H, Sk, num_splits, &ns);
+  if (rc != FA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ns == 1) return run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, 1, nullptr);  // no scratch
+  const size_t need = ws_bytes((int64_t)B * H, D, ns);
+  if (need > kScratchBytes)
+    return fail(FA_ERR_INVALID_ARG, "%zu bytes of partials exceed the %zu-byte static scratch (B*H*ns*(D+1)*4)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FA_OK) return rc;
+  return run_decode(q, k, v, o, lse, B * H, Sk, D, scale, s, ns, ws);
 }
 
 int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_tables,

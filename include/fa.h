@@ -231,6 +231,25 @@ int fa_decode_splitkv_ws(const void* q, const void* k, const void* v, void* o, f
                          void* stream, int num_splits, void* workspace, size_t workspace_bytes);
 
 /*
+ * fa_decode_splitkv_noalloc -- fa_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): same arguments, same kernels and
+ * bit-identical results for the same resolved split count.  It calls no
+ * allocator.  With more than one partition the phase-one partials live in
+ * a static scratch array of 16 MiB (16777216 bytes) that the library's
+ * code object holds on every GPU it runs on until the process ends; a call
+ * whose partials, B*H*ns*(D + 1)*4 bytes rounded up to 256, exceed it
+ * returns FA_ERR_INVALID_ARG before any launch.  Every call on one GPU
+ * shares that GPU's scratch (its contents are whatever the last call left;
+ * phase one overwrites every partial it merges, so nothing needs
+ * clearing): calls that may overlap on one GPU -- on different streams, or
+ * from different threads -- race and must be serialised by the caller.
+ */
+int fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                              void* stream, int num_splits);
+
+/*
  * fa_decode_paged -- fa_decode_splitkv over a paged KV cache ("Adaptive
  * High-Performance Attention Kernels in CUDA", Advanced Production
  * Features, 4. PagedAttention: physical pages [num_blocks, H, block_size, D]

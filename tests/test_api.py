@@ -388,3 +388,17 @@ def test_large_heads_only_through_fa_fwd(lib, D):
     a = dict(GOOD, D=D)
     assert lib.fa_bwd(P[0], P[1], P[2], P[3], P[4], A + 0x5000, A + 0x6000, A + 0x7000, A + 0x8000, a["B"], a["H"],
                       a["Sq"], a["Sk"], D, a["causal"], a["scale"], None) == _capi.FA_ERR_UNSUPPORTED
+
+
+def test_decode_noalloc_rejects_partials_beyond_its_scratch(lib):
+    # 64 * 64 * 4 * 257 * 4 bytes of partials > the 16 MiB static scratch:
+    # refused before any HIP call (fake pointers, explicit split count)
+    a = dict(GOOD, Sq=1)
+    st = lib.fa_decode_splitkv_noalloc(P[0], P[1], P[2], P[3], P[4], 64, 64, 1, 4096, 256, 0, a["scale"], None, 4)
+    assert st == _capi.FA_ERR_INVALID_ARG
+    assert "scratch" in _capi.last_error()
+    # the usual argument checks come first
+    assert lib.fa_decode_splitkv_noalloc(P[0], P[1], P[2], P[3], P[4], 2, 3, 2, 7, 64, 0, 0.125, None, 2) == \
+        _capi.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_splitkv_noalloc(P[0], P[1], P[2], P[3], P[4], 2, 3, 1, 7, 96, 0, 0.125, None, 2) == \
+        _capi.FA_ERR_UNSUPPORTED
