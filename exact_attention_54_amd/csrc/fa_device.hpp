@@ -18,7 +18,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
-// Online softmax: row-max growth (log2 units) tolerated before the reference
+// Online softmax in the prefill: the reference max starts at kMRunInit (far
+// below any score) and moves only when a lane's share of a tile's row sum
+// exceeds kPSumMax, which bounds every p of the tile (p <= 2^15 keeps fp16
+// P finite and at full relative precision).
+constexpr float kMRunInit = -1.0e30f;
+constexpr float kPSumMax = 32768.0f;
+// Split-D forward: row-max growth (log2 units) tolerated before its reference
 // max moves (then O and l are rescaled); in between p <= 2^8.
 constexpr float kLazyRescale = 8.0f;
 
@@ -40,7 +46,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Attention Kernels in CUDA" (Lever B), sized for the 64 x 4-byte LDS bank
 // line of gfx950.
 template <int C>
-__device__ __forceinline__ uint32_t swz(int r, int c) {
+__host__ __device__ __forceinline__ uint32_t swz(int r, int c) {
   static_assert(C == 4 || C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
   if constexpr (C >= 16) {
     const int line = r * (C / 16) + (c >> 4);
@@ -57,7 +63,7 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 // Inverse of swz<C>: the (row, chunk) stored at 16-byte slot `slot` of
 // 256-byte line `line`.
 template <int C>
-__device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
+__host__ __device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
   if constexpr (C >= 16) {
     r = line / (C / 16);
     c = (line % (C / 16)) * 16 + (slot ^ (r & 15));
@@ -74,7 +80,7 @@ __device__ __forceinline__ void swz_inv(int line, int slot, int& r, int& c) {
 // of a 256-byte line.  With 4 chunks per row (D = 32) those 4 rows are one
 // whole line already.
 template <int C>
-__device__ __forceinline__ uint32_t vswz(int r, int c) {
+__host__ __device__ __forceinline__ uint32_t vswz(int r, int c) {
   static_assert(C == 4 || C == 8 || C == 16 || C == 32 || C == 64 || C == 128, "chunks per row");
   if constexpr (C == 4) {
     return (uint32_t)(r * 64 + c * 16);
@@ -89,7 +95,7 @@ __device__ __forceinline__ uint32_t vswz(int r, int c) {
   }
 }
 template <int C>
-__device__ __forceinline__ void vswz_inv(int line, int slot, int& r, int& c) {
+__host__ __device__ __forceinline__ void vswz_inv(int line, int slot, int& r, int& c) {
   if constexpr (C == 4) {
     r = line * 4 + slot / 4;
     c = slot % 4;

@@ -12,14 +12,17 @@
 //                 transposed product puts one query row in each lane (lanes
 //                 l and l+32 share a row), so the row max needs one
 //                 cross-half exchange and the row sum none until the end.
-//   online softmax  m_new = max(m, rowmax), p = 2^(s*c - m), l += rowsum(p),
-//                 with c = scale*log2(e) folded into one FMA per score
-//                 ("FlashAttention-2 MMA", Technical Details, Online Softmax).
-//                 The reference max m only moves when a row max grows by
-//                 more than 2^8 (then O and l are rescaled by 2^(m - m_new));
-//                 in between p <= 2^8, well inside fp16's range and at its
-//                 full relative precision, so only rounding differs and the
-//                 rescale is rare.
+//   online softmax  p = 2^(s*c - m), l += rowsum(p), with c = scale*log2(e)
+//                 folded into one FMA per score ("FlashAttention-2 MMA",
+//                 Technical Details, Online Softmax).  The reference max m
+//                 is not taken per tile: a lane's share of the tile's row
+//                 sum bounds every p it formed, so while that share stays
+//                 <= 2^15 P is inside fp16's range at full relative
+//                 precision and m stays.  When it does not (a row's first
+//                 tile, or a row max that grew by ~2^15) m moves to the
+//                 tile's row max, O and l are rescaled by 2^(m - m_new) and
+//                 P is formed again.  Only rounding differs from moving m on
+//                 every tile.
 //   O^T += V^T P^T  P is rounded to fp16 in registers and used directly as
 //                 the B operand: the accumulator layout of S^T lists keys
 //                 8*(j/4) + 4*(l/32) + j%4, and the contraction index is
@@ -287,57 +290,80 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
-  float m_run = kNegInf;  // reference max of s*c (log2 units) of this lane's row
-  float m_cand = kNegInf; // reference max wanted by the next tile
-  bool grow = false;      // m_cand > m_run: O and l need the rescale first
-  float l_run = 0.f;      // this lane's share of the row sum
+  // Reference max of s*c (log2 units) of this lane's row: the first tile's
+  // row max, or far below any score for a row without a visible key there
+  // (a later tile with one then moves it, and a masked score still gives
+  // exp2(-inf) = 0); it moves only when the P of a tile could leave fp16's
+  // range (see refit).
+  float m_run = kMRunInit;
+  float l_run = 0.f;  // this lane's share of the row sum
   f32x16 s_cur[C::NKB];
 
-  // Masks S^T of key tile kt (keys past Sk, and keys after the row when
-  // causal; only instantiated for tiles that need it), then decides whether
-  // the reference max must move for it.
-  auto mask_and_max = [&](f32x16 (&s)[C::NKB], int kt, auto mask_tag) {
-    if constexpr (decltype(mask_tag)::value) {
-      const int kbase = kt * BN;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kbase + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (key >= Sk || (CAUSAL && key > qi)) s[kb][j] = kNegInf;
-        }
-    }
-    float mx = kNegInf;
+  // Masks S^T of key tile kt: keys past Sk, and keys after the row when
+  // causal (only instantiated for tiles that need it).
+  auto mask_tile = [&](f32x16 (&s)[C::NKB], int kt) {
+    const int kbase = kt * BN;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[kb][j]), s[kb][j + 1]);  // v_max3
-    const float mt = xhalf_max(mx) * c2;
-    grow = mt > m_run + kLazyRescale;
-    m_cand = grow ? mt : m_run;
+      for (int j = 0; j < 16; ++j) {
+        const int key = kbase + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+        if (key >= Sk || (CAUSAL && key > qi)) s[kb][j] = kNegInf;
+      }
+  };
+  // p = 2^(s*c - m_run) rounded to fp16 into the B operand of P V; returns
+  // this lane's share of the tile's row sum (of the fp16 P that feeds P V).
+  auto softmax_tile = [&](f32x16 (&s)[C::NKB], h8 (&pop)[C::NKB][2]) {
+    float t = 0.f;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        h2 pr;
+        pr[0] = (_Float16)exp2_fast(__builtin_fmaf(s[kb][j], c2, -m_run));
+        pr[1] = (_Float16)exp2_fast(__builtin_fmaf(s[kb][j + 1], c2, -m_run));
+        t = dot2(pr, ones, t);
+        pop[kb][j >> 3][j & 7] = pr[0];
+        pop[kb][j >> 3][(j & 7) + 1] = pr[1];
+      }
+    return t;
+  };
+  // Every p is at most a lane's share t of the row sum, so t <= kPSumMax
+  // keeps P inside fp16's range at full relative precision.  Otherwise
+  // (rare: the first tile of a row, or a row max that grew by more than
+  // ~2^15 over the reference) the reference moves to the tile's row max
+  // (the online-softmax rescale of O and l by 2^(m_old - m_new)) and P is
+  // formed again.
+  auto refit = [&](f32x16 (&s)[C::NKB], h8 (&pop)[C::NKB][2], float& t) {
+    if (__builtin_expect(wave_any(!(t <= kPSumMax)), 0)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s[kb][j]), s[kb][j + 1]);
+      const float m_new = fmaxf(m_run, xhalf_max(mx) * c2);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 before the row's first visible key
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m_run = m_new;
+      t = softmax_tile(s, pop);
+    }
   };
 
-  // One pipelined step on tile kt, a single basic block: exp/convert/sum of
-  // S(kt) issued together with the MFMAs of S(kt+1) (when NEXT), then
-  // O += P(kt) V(kt) issued together with the mask and row max of S(kt+1).
-  auto step = [&](int kt, auto mask_next, auto next_tag) {
+  // One pipelined step on tile kt: exp/convert/sum of S(kt) issued together
+  // with the MFMAs of S(kt+1) (when NEXT, into s_n), then O += P(kt) V(kt),
+  // and the mask of S(kt+1) when the next tile needs one.
+  auto step = [&](int kt, f32x16 (&s_c)[C::NKB], f32x16 (&s_n)[C::NKB], auto mask_next, auto next_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     h8 pop[C::NKB][2];
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        h2 pr;
-        pr[0] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[kb][j], c2, -m_use));
-        pr[1] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[kb][j + 1], c2, -m_use));
-        l_run = dot2(pr, ones, l_run);  // row sum of the fp16 P that feeds P V
-        pop[kb][j >> 3][j & 7] = pr[0];
-        pop[kb][j >> 3][(j & 7) + 1] = pr[1];
-      }
-    f32x16 s_nxt[C::NKB];
-    if constexpr (NEXT) qk((kt + 1) & 1, s_nxt);
+    float t = softmax_tile(s_c, pop);
+    if constexpr (NEXT) qk((kt + 1) & 1, s_n);
+    refit(s_c, pop, t);
+    l_run += t;
 
     const char* Vs = smem + C::V_BASE + (kt & 1) * C::TILE_BYTES;
 #pragma unroll
@@ -353,45 +379,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
           const h8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           oacc[db] = mfma_32x32x16(a, pop[kb][k2], oacc[db]);
         }
-    if constexpr (NEXT) {
-      mask_and_max(s_nxt, kt + 1, mask_next);
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_nxt[kb];
-    }
-  };
-  // The same step for the hot part of the loop: the next tile needs no
-  // mask and S(kt+1) goes to the other register set (no copy).
-  auto step_clean = [&](int kt, f32x16 (&s_c)[C::NKB], f32x16 (&s_n)[C::NKB]) {
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    h8 pop[C::NKB][2];
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        h2 pr;
-        pr[0] = (_Float16)exp2_fast(__builtin_fmaf(s_c[kb][j], c2, -m_use));
-        pr[1] = (_Float16)exp2_fast(__builtin_fmaf(s_c[kb][j + 1], c2, -m_use));
-        l_run = dot2(pr, ones, l_run);
-        pop[kb][j >> 3][j & 7] = pr[0];
-        pop[kb][j >> 3][(j & 7) + 1] = pr[1];
-      }
-    qk((kt + 1) & 1, s_n);
-    const char* Vs = smem + C::V_BASE + (kt & 1) * C::TILE_BYTES;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int key = 32 * kb + 16 * k2 + v_key;
-          const int chunk = 4 * db + v_chunk;
-          const h4v lo = lds_read_tr16(Vs + vswz<C::KCH>(key, chunk) + v_half);
-          const h4v hi = lds_read_tr16(Vs + vswz<C::KCH>(key + 8, chunk) + v_half);
-          const h8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = mfma_32x32x16(a, pop[kb][k2], oacc[db]);
-        }
-    mask_and_max(s_n, kt + 1, std::false_type{});
+    if constexpr (NEXT && decltype(mask_next)::value) mask_tile(s_n, kt + 1);
   };
   auto tile_needs_mask = [&](int kt) { return (kt * BN + BN > Sk) || (CAUSAL && kt * BN + BN - 1 > qw); };
 
@@ -405,26 +393,21 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   __syncthreads();
   if (jlast >= kb) {
     qk(kb & 1, s_cur);
-    if (tile_needs_mask(kb)) mask_and_max(s_cur, kb, std::true_type{});
-    else mask_and_max(s_cur, kb, std::false_type{});
+    if (tile_needs_mask(kb)) mask_tile(s_cur, kb);
+    // the reference starts at the first tile's row max (a row without a
+    // visible key there keeps kMRunInit), so its P needs no refit
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb2 = 0; kb2 < C::NKB; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s_cur[kb2][j]), s_cur[kb2][j + 1]);
+    m_run = fmaxf(xhalf_max(mx) * c2, kMRunInit);
   }
   __syncthreads();  // K stage 0 is refilled with K(2) below
 
   auto begin_tile = [&](int kt) {
     if (kt + 2 < ke) load_k(kt + 2, kt & 1);
     if (kt + 1 < ke) load_v(kt + 1, (kt + 1) & 1);
-  };
-  auto rescale_if_grown = [&]() {
-    if (wave_any(grow)) {  // rare: some row max grew by more than 2^8
-      const float alpha = exp2_fast(m_run - m_cand);  // 1 where the max stays, 0 on a row's first tile
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-      m_run = m_cand;
-      grow = false;
-    }
   };
   auto end_tile = [&]() {
     wait_vmem_all();
@@ -440,28 +423,27 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   int kt = kb;
   for (; kt + 2 <= kclean; kt += 2) {
     begin_tile(kt);
-    rescale_if_grown();
-    step_clean(kt, s_cur, s_alt);
+    step(kt, s_cur, s_alt, std::false_type{}, std::true_type{});
     end_tile();
     begin_tile(kt + 1);
-    rescale_if_grown();
-    step_clean(kt + 1, s_alt, s_cur);
+    step(kt + 1, s_alt, s_cur, std::false_type{}, std::true_type{});
     end_tile();
   }
-  // The last few tiles (diagonal, ragged tail, past this wavefront's rows).
-  for (; kt < ke; ++kt) {
+  // The last few tiles (diagonal, ragged tail, past this wavefront's rows):
+  // the next tile's scores are always masked here (the mask leaves a tile
+  // that needs none unchanged), and the final tile has no next one.
+  for (; kt + 1 < ke; ++kt) {
     begin_tile(kt);
     if (kt <= jlast) {
-      rescale_if_grown();
-      // the mask of S(kt+1) is a compile-time variant, so unmasked tiles
-      // carry no compare/select work
-      if (kt + 1 < ke) {
-        if (tile_needs_mask(kt + 1)) step(kt, std::true_type{}, std::true_type{});
-        else step(kt, std::false_type{}, std::true_type{});
-      } else {
-        step(kt, std::false_type{}, std::false_type{});
-      }
+      step(kt, s_cur, s_alt, std::true_type{}, std::true_type{});
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_alt[kb];
     }
+    end_tile();
+  }
+  if (kt < ke) {
+    begin_tile(kt);
+    if (kt <= jlast) step(kt, s_cur, s_alt, std::false_type{}, std::false_type{});
     end_tile();
   }
 
