@@ -46,12 +46,14 @@ struct SplitDCfg {
   static_assert(PER == 2 || PER == 4, "reduction piece");
 };
 
-// Float offset of element j of lane L's 16 partial scores: four 16-byte
-// chunks per lane, chunk c stored at c ^ ((L >> 2) & 3), so 16 lanes reading
-// the same chunk touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int red_off(int L, int j) {
-  return L * 16 + (((j >> 2) ^ ((L >> 2) & 3)) << 2) + (j & 3);
-}
+// Float offset of element j of lane L's 16 partial scores: chunk-major,
+// 16-byte chunk c of every lane in one contiguous 1 KiB run, so the 64 lanes
+// writing (or reading back) one chunk touch 64 consecutive 16-byte slots.
+// (A lane-major layout with the chunks XOR-permuted reads without bank
+// conflicts on gfx950 but costs 8 conflict cycles per 16-byte write, as
+// measured with SQ_LDS_BANK_CONFLICT.)  The flat offsets 0..1023 also
+// partition the tile for the reduce-scatter into contiguous pieces.
+__device__ __forceinline__ int red_off(int L, int j) { return (j >> 2) * 256 + L * 4 + (j & 3); }
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * (D / 128), 1)
@@ -125,9 +127,9 @@ fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K
   const int v_half = (ti & 1) * 8;
 
   // the piece of the score tile this wavefront sums: PER consecutive floats
-  // per lane starting at flat index w * 1024 / NW + lane * PER
-  const int pf = w * (1024 / NW) + lane * C::PER;
-  const int pofs = red_off(pf >> 4, pf & 15);
+  // per lane starting at flat offset w * 1024 / NW + lane * PER (red_off is
+  // chunk-major, so the pieces of consecutive lanes are contiguous)
+  const int pofs = w * (1024 / NW) + lane * C::PER;
 
   f32x16 oacc[4];
 #pragma unroll
