@@ -5,9 +5,9 @@
 Produces ``exact_attention_54_amd/libfa_hip.so`` from ``csrc/fa_api.hip``
 (the C ABI of ``include/fa.h`` plus every kernel), the streaming-read /
 MFMA loop probes ``exact_attention_54_amd/libroofline_probe.so`` from
-``csrc/roofline_probe.hip`` that bench.py reports as context, and the
-test-only MFMA layout probe ``tests/hip/libmfma_probe.so``.  Always
-recompiles.
+``csrc/roofline_probe.hip`` that bench.py reports as context, the test-only
+MFMA layout probe ``tests/hip/libmfma_probe.so`` and the host-side LDS
+layout check ``tests/hip/libswizzle_check.so``.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -91,8 +91,18 @@ def build_roofline_probe(verbose: bool = False) -> str:
     return compile_shared([ROOFLINE_SRC], ROOFLINE_LIB, verbose=verbose)
 
 
+SWIZZLE_SRC = os.path.join(ROOT, "tests", "hip", "swizzle_check.hip")
+SWIZZLE_LIB = os.path.join(ROOT, "tests", "hip", "libswizzle_check.so")
+
+
+def build_swizzle_check(verbose: bool = False) -> str:
+    """Host-side check of the kernels' LDS layouts, used by tests/test_swizzle.py."""
+    return compile_shared([SWIZZLE_SRC], SWIZZLE_LIB, include_dirs=[CSRC], verbose=verbose)
+
+
 def build_all(verbose: bool = False):
-    return [build_library(verbose), build_test_probe(verbose), build_roofline_probe(verbose)]
+    return [build_library(verbose), build_test_probe(verbose), build_roofline_probe(verbose),
+            build_swizzle_check(verbose)]
 
 
 if __name__ == "__main__":

@@ -171,6 +171,15 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
   return best;
 }
 
+// Launches an instantiation of fa::fwd_kernel (its LDS is static).
+template <int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool KSPLIT, class... Args>
+int launch_fwd_kernel(unsigned grid, hipStream_t stream, const char* what, Args... args) {
+  using Cfg = fa::FwdCfg<D, BN, NW>;
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, VARLEN, KSPLIT>), dim3(grid), dim3(Cfg::THREADS), 0, stream,
+                     args...);
+  return launched(what);
+}
+
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
                      float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
@@ -183,11 +192,10 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
   ksp.ns = pl.ns;
   ksp.ws_o = static_cast<float*>(ws);
   ksp.ws_lse = ksp.ws_o + (size_t)rows * pl.ns * D;
-  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, false, true>), dim3((unsigned)pl.grid),
-                     dim3(Cfg::THREADS), 0, stream, static_cast<const _Float16*>(q),
-                     static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o),
-                     lse, Sq, Sk, BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
-  int rc = launched("fa_fwd key-split kernel launch");
+  int rc = launch_fwd_kernel<D, BN, NW, CAUSAL, false, true>(
+      (unsigned)pl.grid, stream, "fa_fwd key-split kernel launch", static_cast<const _Float16*>(q),
+      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk,
+      BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
   if (rc == FA_OK) {
     constexpr int R = fa::MergeCfg<D>::ROWS;
     hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
@@ -204,11 +212,10 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   using Cfg = fa::FwdCfg<D, BN, NW>;
   if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL>), dim3(nqt * BH), dim3(Cfg::THREADS), 0, stream,
-                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH, nqt,
-                     scale * fa::kLog2e);
-  return launched("fa_fwd kernel launch");
+  return launch_fwd_kernel<D, BN, NW, CAUSAL, false, false>(
+      (unsigned)(nqt * BH), stream, "fa_fwd kernel launch", static_cast<const _Float16*>(q),
+      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH,
+      nqt, scale * fa::kLog2e, fa::VarlenArgs{}, fa::KeySplit{});
 }
 
 // The tile kernel of head dim D with the geometry the plan chose: D = 256
@@ -236,11 +243,10 @@ int launch_fwd_varlen(const void* q, const void* k, const void* v, void* o, floa
   const int64_t BH = (int64_t)B * va.H;
   const int64_t grid = (BH + 7) / 8 * 8 * nqt;  // slice count rounded up to a multiple of 8 (one per XCD)
   if (grid > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  const float c2 = scale * fa::kLog2e;
-  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0, stream,
-                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                     static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, 0, 0, (int)BH, nqt, c2, va);
-  return launched("fa_fwd_varlen kernel launch");
+  return launch_fwd_kernel<D, BN, NW, CAUSAL, true, false>(
+      (unsigned)grid, stream, "fa_fwd_varlen kernel launch", static_cast<const _Float16*>(q),
+      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, 0, 0,
+      (int)BH, nqt, scale * fa::kLog2e, va, fa::KeySplit{});
 }
 
 template <int D, bool CAUSAL>
@@ -367,13 +373,30 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
                      static_cast<const _Float16*>(o), dO, lse, dvec, l2, rows);
   int rc = launched("fa_bwd preprocess launch");
   if (rc != FA_OK) return rc;
-  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, NW, CAUSAL>), dim3((unsigned)kv_grid), dim3(64 * NW), 0, stream, Q, K, V,
-                     dO, l2, dvec, static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), Sq, Sk, BH,
-                     (int)(kv_grid / BH), scale);
+  // dynamic LDS; above 64 KiB (D = 256) the kernels must be allowed it first
+  constexpr int kv_dyn = fa::dkdv_lds_bytes<D, NW>();
+  constexpr int q_dyn = fa::dq_lds_bytes<D, NW>();
+  static_assert(kv_dyn <= 160 * 1024 && q_dyn <= 160 * 1024, "LDS budget per CU");
+  auto* kv_kern = &fa::bwd_dkdv_kernel<D, NW, CAUSAL>;
+  auto* q_kern = &fa::bwd_dq_kernel<D, NW, CAUSAL>;
+  if constexpr (kv_dyn > 65536) {
+    rc = hip_check(hipFuncSetAttribute(reinterpret_cast<const void*>(kv_kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kv_dyn),
+                   "fa_bwd LDS size attribute");
+    if (rc != FA_OK) return rc;
+  }
+  if constexpr (q_dyn > 65536) {
+    rc = hip_check(hipFuncSetAttribute(reinterpret_cast<const void*>(q_kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, q_dyn),
+                   "fa_bwd LDS size attribute");
+    if (rc != FA_OK) return rc;
+  }
+  hipLaunchKernelGGL(kv_kern, dim3((unsigned)kv_grid), dim3(64 * NW), kv_dyn, stream, Q, K, V, dO, l2, dvec,
+                     static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), Sq, Sk, BH, (int)(kv_grid / BH), scale);
   rc = launched("fa_bwd dK/dV launch");
   if (rc != FA_OK) return rc;
-  hipLaunchKernelGGL((fa::bwd_dq_kernel<D, NW, CAUSAL>), dim3((unsigned)q_grid), dim3(64 * NW), 0, stream, Q, K, V, dO,
-                     l2, dvec, static_cast<_Float16*>(dq), Sq, Sk, BH, nqt, scale);
+  hipLaunchKernelGGL(q_kern, dim3((unsigned)q_grid), dim3(64 * NW), q_dyn, stream, Q, K, V, dO, l2, dvec,
+                     static_cast<_Float16*>(dq), Sq, Sk, BH, nqt, scale);
   return launched("fa_bwd dQ launch");
 }
 
@@ -748,7 +771,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
-  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 64 and 128");
+  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 32, 64, 128 and 256");
   if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;
@@ -760,12 +783,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (rc != FA_OK) return rc;
   float* dvec = static_cast<float*>(ws);
   const int BH = B * H;
-  if (D == 64)
-    rc = causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
-  else
-    rc = causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+  switch (D) {
+    case 32:
+      rc = causal ? launch_bwd<32, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                  : launch_bwd<32, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+      break;
+    case 64:
+      rc = causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                  : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+      break;
+    case 128:
+      rc = causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                  : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+      break;
+    default:
+      rc = causal ? launch_bwd<256, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                  : launch_bwd<256, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+      break;
+  }
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
 }

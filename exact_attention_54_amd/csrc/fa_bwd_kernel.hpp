@@ -40,27 +40,36 @@ namespace fa {
 // one chunk column) and by ds_read_b64_tr_b16 (4 consecutive rows x 4
 // consecutive chunks): the XOR key swaps the two 2-bit halves of the row
 // index, which keeps both groups of 16 chunks on 16 distinct 16-byte bank
-// groups of a 256-byte line.
+// groups of a 256-byte line.  Rows of 4 chunks (D = 32) share a line four
+// at a time, and XOR the chunk with the line index instead.
 template <int C>
-__device__ __forceinline__ uint32_t bswz(int r, int c) {
-  static_assert(C == 8 || C == 16, "chunks per row");
-  if constexpr (C == 16) {
+__host__ __device__ __forceinline__ uint32_t bswz(int r, int c) {
+  static_assert(C == 4 || C == 8 || C == 16 || C == 32, "chunks per row");
+  if constexpr (C >= 16) {
+    const int line = r * (C / 16) + (c >> 4);
     const int slot = (c & 15) ^ (((r & 3) << 2) | ((r >> 2) & 3));
-    return (uint32_t)(r * 256 + slot * 16);
-  } else {
+    return (uint32_t)(line * 256 + slot * 16);
+  } else if constexpr (C == 8) {
     const int line = r >> 1;
     const int slot = (r & 1) * 8 + (c ^ (((line & 1) << 2) | ((line >> 1) & 3)));
+    return (uint32_t)(line * 256 + slot * 16);
+  } else {
+    const int line = r >> 2;
+    const int slot = (r & 3) * 4 + (c ^ (line & 3));
     return (uint32_t)(line * 256 + slot * 16);
   }
 }
 template <int C>
-__device__ __forceinline__ void bswz_inv(int line, int slot, int& r, int& c) {
-  if constexpr (C == 16) {
-    r = line;
-    c = slot ^ (((r & 3) << 2) | ((r >> 2) & 3));
-  } else {
+__host__ __device__ __forceinline__ void bswz_inv(int line, int slot, int& r, int& c) {
+  if constexpr (C >= 16) {
+    r = line / (C / 16);
+    c = (line % (C / 16)) * 16 + (slot ^ (((r & 3) << 2) | ((r >> 2) & 3)));
+  } else if constexpr (C == 8) {
     r = line * 2 + slot / 8;
     c = (slot % 8) ^ (((line & 1) << 2) | ((line >> 1) & 3));
+  } else {
+    r = line * 4 + slot / 4;
+    c = (slot % 4) ^ (line & 3);
   }
 }
 
@@ -153,6 +162,13 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
   }
 }
 
+// Workgroups per CU the register budget is sized for: two below D = 256;
+// at D = 256 the fp32 gradient accumulators of a wavefront alone take 256
+// registers per lane, so one (the wavefront then has the SIMD's whole
+// register file).
+template <int D>
+constexpr int bwd_wg_per_cu() { return D > 128 ? 1 : 2; }
+
 // --------------------------------------------------------------- dK and dV
 
 // LDS: the workgroup's V rows (32 NW x D fp16, swz), then per stage a Q
@@ -166,15 +182,21 @@ struct DkdvLds {
   static constexpr int BYTES = VROWS + 2 * STAGE;
 };
 
+// LDS bytes of a workgroup (dynamic LDS, passed at launch; above 64 KiB,
+// at D = 256, the kernel must be allowed that much first).
+template <int D, int NW>
+constexpr int dkdv_lds_bytes() {
+  return (DkdvLds<D, NW>::BYTES > NW * 32 * D * 2) ? DkdvLds<D, NW>::BYTES : NW * 32 * D * 2;
+}
+
 template <int D, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, bwd_wg_per_cu<D>())
 bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, const _Float16* __restrict__ V,
                 const _Float16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                 _Float16* __restrict__ dK, _Float16* __restrict__ dV, int Sq, int Sk, int BH, int nkt, float scale) {
   using C = BwdCfg<D, NW>;
   using L = DkdvLds<D, NW>;
-  constexpr int EPI = NW * 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[(L::BYTES > EPI) ? L::BYTES : EPI];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];  // dkdv_lds_bytes<D, NW>(), passed at launch
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -348,8 +370,13 @@ struct DqLds {
   static constexpr int BYTES = 4 * TILE;  // K0 K1 V0 V1
 };
 
+template <int D, int NW>
+constexpr int dq_lds_bytes() {
+  return (DqLds<D>::BYTES > NW * 32 * D * 2) ? DqLds<D>::BYTES : NW * 32 * D * 2;
+}
+
 template <int D, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, bwd_wg_per_cu<D>())
 bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, const _Float16* __restrict__ V,
               const _Float16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
               _Float16* __restrict__ dQ, int Sq, int Sk, int BH, int nqt, float scale) {
@@ -357,8 +384,7 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
   using L = DqLds<D>;
   constexpr int BN = L::BN;
   constexpr int NKB = BN / 32;
-  constexpr int EPI = NW * 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[(L::BYTES > EPI) ? L::BYTES : EPI];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];  // dq_lds_bytes<D, NW>(), passed at launch
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -145,9 +145,9 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
  * caller-owned device memory, 16-byte aligned (lse 4-byte); outputs must not
  * overlap inputs.  A per-row workspace (D and the LSE in log2 units,
  * 2*B*H*Sq fp32) comes from the same
- * per-device pool as fa_decode_splitkv.  Four kernels run on `stream`.
- * Supports D in {64, 128} (other D: FA_ERR_UNSUPPORTED); other errors as
- * fa_fwd.
+ * per-device pool as fa_decode_splitkv.  Three kernels run on `stream`.
+ * Supports D in {32, 64, 128, 256} (other D: FA_ERR_UNSUPPORTED); other
+ * errors as fa_fwd.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,

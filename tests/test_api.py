@@ -370,7 +370,7 @@ def bwd(lib, **kw):
                       a["Sq"], a["Sk"], a["D"], a["causal"], a["scale"], None)
 
 
-@pytest.mark.parametrize("D", [16, 32, 48, 96, 256, 512, 1024])
+@pytest.mark.parametrize("D", [16, 48, 96, 512, 1024])
 def test_bwd_rejects_head_dims_without_a_kernel(lib, D):
     # every head dim the backward has no kernel for is refused before any HIP
     # call (the fake pointers are never touched)
