@@ -40,7 +40,7 @@ PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd TFLOPS (causal prefill D=128) + decode K/V GB/s, % of roofline"
 KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_kernel.hpp", "fa_splitd_kernel.hpp", "fa_decode_kernel.hpp", "fa_bwd_kernel.hpp",
-                  "fa_api.hip"]
+                  "fa_api.hip", "fa_fwd256.hip"]
 
 
 def log(msg):
@@ -55,7 +55,7 @@ def kernel_source_hash():
     from exact_attention_54_amd import build as fa_build
 
     h = hashlib.sha256()
-    h.update(repr(fa_build.COMMON_FLAGS + fa_build.LIB_FLAGS).encode())
+    h.update(repr((fa_build.COMPILE_FLAGS, fa_build.LIB_FLAGS, fa_build.LIB_UNITS)).encode())
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "exact_attention_54_amd", "csrc", name), encoding="utf-8") as f:
             for line in f:

@@ -23,16 +23,16 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_hip.so")
 
 ARCH = "gfx950"
-COMMON_FLAGS = [
+COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+COMMON_FLAGS = COMPILE_FLAGS + ["-shared"]
 
 
 def hipcc() -> str:
@@ -72,9 +72,43 @@ PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
 LIB_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 
 
+# The library's translation units and the flags each adds to LIB_FLAGS: the
+# D = 256 prefill kernels keep their MFMA results in VGPRs (see
+# csrc/fa_fwd256.hip), which the two-wavefront-per-SIMD kernels do not want.
+LIB_UNITS = [
+    ("fa_api.hip", []),
+    ("fa_fwd256.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+]
+
+
+def run_hipcc(cmd, verbose=False):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature name; that warning is expected
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+
+
 def build_library(verbose: bool = False) -> str:
-    return compile_shared([os.path.join(CSRC, "fa_api.hip")], LIB, include_dirs=[INCLUDE, CSRC], extra=LIB_FLAGS,
-                          verbose=verbose)
+    """Each unit compiled to an object with its own flags, then linked."""
+    objs = []
+    for name, extra in LIB_UNITS:
+        obj = os.path.join(CSRC, os.path.splitext(name)[0] + ".o")
+        cmd = [hipcc(), *COMPILE_FLAGS, *LIB_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, name), "-o", obj]
+        run_hipcc(cmd, verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    run_hipcc([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    for obj in objs:
+        os.remove(obj)
+    os.replace(tmp, LIB)
+    return LIB
 
 
 def build_test_probe(verbose: bool = False) -> str:

@@ -20,6 +20,22 @@
 #include "fa_fwd_kernel.hpp"
 #include "fa_splitd_kernel.hpp"
 
+namespace fa {
+// The D = 256 prefill kernels are compiled in fa_fwd256.hip (with MFMA
+// results in VGPRs); here they are only launched.
+#define FA_FWD256_EXTERN(CAUSAL, VARLEN, KSPLIT)                                                                 \
+  extern template __global__ void fwd_kernel<256, 32, 4, CAUSAL, VARLEN, KSPLIT>(                                \
+      const _Float16* __restrict__, const _Float16* __restrict__, const _Float16* __restrict__,                  \
+      _Float16* __restrict__, float* __restrict__, int, int, int, int, float, VarlenArgs, KeySplit);
+FA_FWD256_EXTERN(false, false, false)
+FA_FWD256_EXTERN(true, false, false)
+FA_FWD256_EXTERN(false, false, true)
+FA_FWD256_EXTERN(true, false, true)
+FA_FWD256_EXTERN(false, true, false)
+FA_FWD256_EXTERN(true, true, false)
+#undef FA_FWD256_EXTERN
+}  // namespace fa
+
 namespace {
 
 thread_local char g_err[512] = "";

@@ -218,6 +218,12 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   h8 qreg[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_h8(buf_load16(rq, ((uint32_t)qi * RS + 16 * ks + 8 * hh) * 2u));
+  if constexpr (D == 256) {
+    // one wavefront per SIMD: Q (64 registers), only ever an MFMA operand,
+    // stays in the accumulation registers and the VGPRs hold O, S and P
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) asm volatile("" : "+a"(qreg[ks]));
+  }
 
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + C::BM, Sk) + BN - 1) / BN) : nkt_all;
