@@ -602,7 +602,7 @@ struct FwdPlan {
   size_t ws = 0;  // workspace bytes (0: none)
 };
 
-int plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, FwdPlan* out) {
+int compute_plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, FwdPlan* out) {
   FwdPlan p;
   const int64_t BH = (int64_t)B * H;
   if (BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
@@ -639,6 +639,51 @@ int plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, FwdPlan*
     if (p.nw == 4) p.sp = plan_fwd_split((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus);
     if (p.sp.ns > 1) p.ws = ws_bytes(BH * (nqt - p.sp.ts) * BM, D, p.sp.ns);
   }
+  *out = p;
+  return FA_OK;
+}
+
+// Plans depend only on the sizes and the CU count, and the key-split
+// planner simulates every candidate dispatch (hundreds of microseconds on
+// the host for a 256-workgroup grid), so plans are cached: a direct-mapped
+// table of recent sizes, shared by all threads under one mutex.
+struct PlanKey {
+  int B, H, Sq, Sk, D, causal, cus;
+  bool operator==(const PlanKey& o) const {
+    return B == o.B && H == o.H && Sq == o.Sq && Sk == o.Sk && D == o.D && causal == o.causal && cus == o.cus;
+  }
+};
+struct PlanSlot {
+  bool used = false;
+  PlanKey key{};
+  FwdPlan plan;
+};
+constexpr int kPlanSlots = 256;
+std::mutex g_plan_mu;
+PlanSlot g_plans[kPlanSlots];
+
+int plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, FwdPlan* out) {
+  const PlanKey key{B, H, Sq, Sk, D, causal ? 1 : 0, cus};
+  uint64_t h = 1469598103934665603ull;  // FNV-1a over the seven sizes
+  for (int x : {B, H, Sq, Sk, D, key.causal, cus}) {
+    h ^= (uint32_t)x;
+    h *= 1099511628211ull;
+  }
+  PlanSlot& slot = g_plans[h % kPlanSlots];
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    if (slot.used && slot.key == key) {
+      *out = slot.plan;
+      return FA_OK;
+    }
+  }
+  FwdPlan p;
+  const int rc = compute_plan_fwd(B, H, Sq, Sk, D, causal, cus, &p);
+  if (rc != FA_OK) return rc;  // invalid sizes are not cached: the error message is set again each call
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  slot.used = true;
+  slot.key = key;
+  slot.plan = p;
   *out = p;
   return FA_OK;
 }

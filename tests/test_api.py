@@ -208,6 +208,42 @@ def test_fwd_key_splits_properties_on_random_shapes(lib):
     assert lib.fa_fwd_key_splits(1, 1, 5, 5, 48, 1, 256) == 0
 
 
+def test_fwd_plan_cache_is_transparent(lib):
+    # plans are cached per size tuple in a table of 256 slots: 1200 shapes
+    # (every slot reused several times) queried in one order and again in
+    # another give identical answers
+    import numpy as np
+
+    g = np.random.Generator(np.random.PCG64(11))
+    shapes = []
+    for _ in range(1200):
+        shapes.append((int(g.integers(1, 5)), int(g.integers(1, 33)), int(g.integers(1, 9000)),
+                       int(g.integers(1, 9000)), int(g.choice([32, 64, 128, 256, 512, 1024])),
+                       int(g.integers(0, 2)), int(g.choice([80, 256, 304]))))
+
+    def answers(order):
+        return {shapes[i]: (lib.fa_fwd_key_splits(*shapes[i]), lib.fa_fwd_workspace_bytes(*shapes[i]))
+                for i in order}
+
+    first = answers(range(len(shapes)))
+    again = answers(g.permutation(len(shapes)))
+    assert first == again
+
+
+def test_fwd_plan_is_cheap_once_cached(lib):
+    # the key-split planner simulates its candidate dispatches; a repeated
+    # size tuple must not pay for that again (uncached: hundreds of us here)
+    import time
+
+    args = (1, 16, 2048, 2048, 256, 1, 256)
+    lib.fa_fwd_workspace_bytes(*args)
+    t0 = time.perf_counter()
+    for _ in range(200):
+        lib.fa_fwd_workspace_bytes(*args)
+    per_call_us = (time.perf_counter() - t0) / 200 * 1e6
+    assert per_call_us < 50, per_call_us
+
+
 def rup256(n):
     return -(-n // 256) * 256
 
