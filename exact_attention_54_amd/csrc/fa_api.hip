@@ -10,6 +10,7 @@
 #include <cmath>
 #include <functional>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 #include <cstdarg>
 #include <cstdint>
@@ -96,40 +97,40 @@ int device_cu_count(int* out);
 int workspace_pool(hipMemPool_t* out);
 size_t ws_bytes(int64_t BH, int D, int ns);
 
-// Key-range split of a small prefill grid (fa::KeySplit): which query tiles
-// to split (ts .. nqt-1) and into how many parts, chosen by simulating the
-// dispatch.  Times are in units of one key tile of one query tile.
+// Key-range split of a small prefill grid (fa::KeySplit).  Parts (D <=
+// 128): query tiles ts .. nqt-1 in ns parts each.  Runs (D = 256): the key
+// tiles of all query tiles cut into `grid` runs (split_start).
 struct SplitPlan {
-  int ts = 0, ns = 1;
-  int64_t grid = 0;
+  int ts = 0, ns = 1;     // parts
+  int chunk = 0, bias = 0;  // runs
+  int units = 0;          // runs: key tiles of one slice
+  int64_t total = 0;      // runs: key tiles of all slices
+  int64_t grid = 0;       // workgroups of the split kernel (0: no split)
+  int max_parts = 1;      // most parts any query tile is cut into
 };
 
-// Cost model of a split plan, per kernel, fitted to timed plans (kernels
-// and merge, rocprofv3 kernel trace):
-//   D = 256, one workgroup per CU: seven plans of the (1, 16, 2048, 2048)
-//     causal shape, all within 6%;
-//   D <= 128, the 4-wavefront kernel: 34 plans over five shapes; with
-//     these constants every shape gets its fastest measured plan or one
-//     within 1% of it (and the shapes where no split paid stay whole).
+// Cost model of a parts plan (D <= 128, the 4-wavefront kernel), fitted to
+// 34 timed plans over five shapes (kernels and merge, rocprofv3 kernel
+// trace): with these constants every shape gets its fastest measured plan
+// or one within 1% of it (and the shapes where no split paid stay whole).
 // A work item costs its key tiles at unit_us each plus item_us of fixed
 // work (Q load, pipeline fill, epilogue); items go, heaviest first, to the
 // CU that frees first; and the whole job takes at least full_load times its
 // mean time per CU (the clock of a fully loaded chip is lower than that of
 // one whose last heavy tiles run alone).
-struct SplitModel {
+struct PartsModel {
   double unit_us, item_us, full_load, min_gain;
   bool causal_only;
 };
 
-SplitModel fwd_split_model(int D) {
-  if (D == 256) return {4.0 * 128 * 32 * 256 / 3.2e6, 3.9, 1.5, 0.9, false};
+PartsModel fwd_parts_model(int D) {
   // a lone 4-wavefront workgroup of 128 rows runs a 64-key tile of D = 128
   // in ~1.2 us; non-causal grids measured no gain from splitting
   return {1.2 * D / 128.0, 3.0, 1.0, 0.7, true};
 }
 
-double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots,
-                      const SplitModel& m) {
+double fwd_parts_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int ts, int ns, int slots,
+                      const PartsModel& m) {
   std::vector<double> finish((size_t)slots, 0.0);  // min-heap of slot finishing times
   double total = 0.0;
   auto push = [&](int units) {
@@ -159,11 +160,11 @@ double fwd_split_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool caus
 // Split only grids of at most two work items per CU, and only when the
 // modelled time plus the merge (its HBM bytes at ~4.5 TB/s, and a launch)
 // beats the unsplit grid by the model's margin.
-SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus) {
+SplitPlan plan_fwd_parts(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus) {
   SplitPlan best;
-  const SplitModel m = fwd_split_model(D);
+  const PartsModel m = fwd_parts_model(D);
   if (cus < 1 || (int64_t)nqt * BH > 2 * (int64_t)cus || (m.causal_only && !causal)) return best;
-  double best_cost = m.min_gain * fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, cus, m);
+  double best_cost = m.min_gain * fwd_parts_time(nqt, BH, BM, BN, Sq, Sk, causal, nqt, 1, cus, m);
   const int starts[4] = {0, nqt / 4, nqt / 2, 3 * nqt / 4};
   const int parts[5] = {2, 3, 4, 6, 8};
   for (int ts : starts) {
@@ -175,16 +176,120 @@ SplitPlan plan_fwd_split(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk,
       const double rows = (double)BH * (nqt - ts) * BM;
       // partials read back, O and LSE written
       const double bytes = rows * (ns * (D + 1) * 4.0 + D * 2.0 + 4.0);
-      const double cost = fwd_split_time(nqt, BH, BM, BN, Sq, Sk, causal, ts, ns, cus, m) + bytes / 4.5e6 + 2.0;
+      const double cost = fwd_parts_time(nqt, BH, BM, BN, Sq, Sk, causal, ts, ns, cus, m) + bytes / 4.5e6 + 2.0;
       if (cost < best_cost) {
         best_cost = cost;
         best.ts = ts;
         best.ns = ns;
         best.grid = grid;
+        best.max_parts = ns;
       }
     }
   }
   return best;
+}
+
+// Cost model of a runs plan (D = 256), from per-workgroup start / end
+// times read inside the kernel (s_memrealtime) on the (1, 16, 2048, 2048,
+// 256) causal grid.  Unsplit: a workgroup takes lone_unit_us per key tile
+// plus lone_first_us (Q and the first K / V tiles, every workgroup loading
+// at once), and the last heavy tiles run at that rate while the light ones
+// have finished.  Runs (every CU busy to the end): unit_us per key tile,
+// first_us for a run's first segment and seg_us for each further one; the
+// merge reads the partials at merge_bw bytes per us after merge_us.
+struct RunsModel {
+  double lone_unit_us, lone_first_us, unit_us, first_us, seg_us, merge_us, merge_bw;
+};
+
+constexpr RunsModel kRunsModel = {0.82, 6.0, 0.92, 7.9, 3.9, 3.0, 4.0e6};
+
+// Makespan of the unsplit grid: query tiles heaviest first, each to the CU
+// that frees first.
+double fwd_unsplit_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int cus, const RunsModel& m) {
+  std::vector<double> finish((size_t)cus, 0.0);  // min-heap of CU finishing times
+  for (int r = 0; r < nqt; ++r) {
+    const int t = causal ? nqt - 1 - r : r;
+    const double w = fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal) * m.lone_unit_us + m.lone_first_us;
+    for (int i = 0; i < BH; ++i) {
+      std::pop_heap(finish.begin(), finish.end(), std::greater<double>());
+      finish.back() += w;
+      std::push_heap(finish.begin(), finish.end(), std::greater<double>());
+    }
+  }
+  return *std::max_element(finish.begin(), finish.end());
+}
+
+// Modelled time of these runs: the slowest run, plus the merge of the cut
+// tiles.  Also reports the most parts of any tile.
+double fwd_runs_time(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int chunk, int bias,
+                     int64_t grid, const RunsModel& m, int* max_parts) {
+  std::vector<double> cost((size_t)grid, 0.0);
+  std::vector<char> started((size_t)grid, 0);
+  int64_t cut_parts = 0;
+  *max_parts = 1;
+  int64_t lin = 0;
+  for (int b = 0; b < BH; ++b)
+    for (int i = 0; i < nqt; ++i) {
+      const int r = fa::split_order(i, nqt);
+      const int u = fa::fwd_tile_units(causal ? nqt - 1 - r : r, BM, BN, Sq, Sk, causal);
+      const int g0 = fa::split_run((int)lin, chunk, bias), g1 = fa::split_run((int)(lin + u - 1), chunk, bias);
+      for (int g = g0; g <= g1; ++g) {
+        const int64_t lo = std::max<int64_t>(lin, fa::split_start(g, chunk, bias));
+        const int64_t hi = std::min<int64_t>(lin + u, fa::split_start(g + 1, chunk, bias));
+        cost[(size_t)g] += (hi - lo) * m.unit_us + (started[(size_t)g] ? m.seg_us : m.first_us);
+        started[(size_t)g] = 1;
+      }
+      if (g1 > g0) cut_parts += g1 - g0 + 1;
+      *max_parts = std::max(*max_parts, g1 - g0 + 1);
+      lin += u;
+    }
+  const double merge = cut_parts ? m.merge_us + (double)cut_parts * BM * (D + 1) * 4.0 / m.merge_bw : 0.0;
+  return *std::max_element(cost.begin(), cost.end()) + merge;
+}
+
+// Split only grids of at most two query tiles per CU, and only when the
+// best modelled runs (one per CU, biases 0 .. chunk / 4) beat the unsplit
+// grid by 10%.
+SplitPlan plan_fwd_runs(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus) {
+  SplitPlan best;
+  const RunsModel& m = kRunsModel;
+  if (cus < 1 || (int64_t)nqt * BH > 2 * (int64_t)cus) return best;
+  int64_t units = 0;
+  for (int t = 0; t < nqt; ++t) units += fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal);
+  const int64_t total = units * BH;
+  if (total > (int64_t)1 << 28) return best;
+  double best_time = 0.9 * fwd_unsplit_time(nqt, BH, BM, BN, Sq, Sk, causal, cus, m);
+  // at least 4 key tiles per run, and no tile in more than 8 parts (what
+  // the merge loads at once): a run holds at least a seventh of the longest
+  // tile
+  int umax = 0;
+  for (int t = 0; t < nqt; ++t) umax = std::max(umax, fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal));
+  const int64_t chunk = std::max<int64_t>(std::max(4, (umax + 6) / 7), (total + cus - 1) / cus);
+  const int step = std::max<int>(1, (int)(chunk / 4) / 8);
+  for (int bias = 0; bias <= chunk / 4; bias += step) {
+    int64_t grid = (total + chunk - 1) / chunk;
+    while (fa::split_start((int)grid, (int)chunk, bias) < total) ++grid;
+    int max_parts = 1;
+    const double t = fwd_runs_time(nqt, BH, BM, BN, D, Sq, Sk, causal, (int)chunk, bias, grid, m, &max_parts);
+    if (t < best_time) {
+      best_time = t;
+      best.chunk = (int)chunk;
+      best.bias = bias;
+      best.units = (int)units;
+      best.total = total;
+      best.grid = grid;
+      best.max_parts = max_parts;
+    }
+  }
+  return best;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of a runs split: the partial O [grid, 2, BM, D] and
+// log2-sum-exp [grid, 2, BM] of every run.
+size_t runs_ws_bytes(int BM, int D, const SplitPlan& pl) {
+  return round256((size_t)pl.grid * 2 * BM * D * 4) + round256((size_t)pl.grid * 2 * BM * 4);
 }
 
 // Launches an instantiation of fa::fwd_kernel (its LDS is static).
@@ -201,32 +306,54 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
                      float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
   using Cfg = fa::FwdCfg<D, BN, NW>;
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-  const int nsplit = nqt - pl.ts;
-  const int64_t rows = (int64_t)BH * nsplit * Cfg::BM;
-  fa::KeySplit ksp;
-  ksp.ts = pl.ts;
-  ksp.ns = pl.ns;
-  ksp.ws_o = static_cast<float*>(ws);
-  ksp.ws_lse = ksp.ws_o + (size_t)rows * pl.ns * D;
-  int rc = launch_fwd_kernel<D, BN, NW, CAUSAL, false, true>(
-      (unsigned)pl.grid, stream, "fa_fwd key-split kernel launch", static_cast<const _Float16*>(q),
-      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk,
-      BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
-  if (rc == FA_OK) {
+  fa::KeySplit ksp = {};
+  if constexpr (fa::split_by_runs<D>()) {
+    ksp.chunk = pl.chunk;
+    ksp.bias = pl.bias;
+    ksp.units = pl.units;
+    ksp.total = (int)pl.total;
+    ksp.ws_o = static_cast<float*>(ws);
+    ksp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)pl.grid * 2 * Cfg::BM * D * 4));
+    int rc = launch_fwd_kernel<D, BN, NW, CAUSAL, false, true>(
+        (unsigned)((pl.grid + 7) / 8 * 8), stream, "fa_fwd split kernel launch", static_cast<const _Float16*>(q),
+        static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk,
+        BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
+    if (rc != FA_OK) return rc;
+    auto merge = [&](auto nparts) {
+      constexpr int NP = decltype(nparts)::value;
+      using M = fa::SplitMergeCfg<D, Cfg::BM, NP>;
+      hipLaunchKernelGGL((fa::fwd_split_merge_kernel<D, Cfg::BM, BN, CAUSAL, NP>), dim3((unsigned)(BH * nqt * M::BLOCKS)),
+                         dim3(M::THREADS), 0, stream, ksp, static_cast<_Float16*>(o), lse, Sq, Sk, nqt);
+      return launched("fa_fwd split merge launch");
+    };
+    if (pl.max_parts <= 2) return merge(std::integral_constant<int, 2>{});
+    if (pl.max_parts <= 4) return merge(std::integral_constant<int, 4>{});
+    return merge(std::integral_constant<int, 8>{});
+  } else {
+    const int nsplit = nqt - pl.ts;
+    const int64_t rows = (int64_t)BH * nsplit * Cfg::BM;
+    ksp.ts = pl.ts;
+    ksp.ns = pl.ns;
+    ksp.ws_o = static_cast<float*>(ws);
+    ksp.ws_lse = ksp.ws_o + (size_t)rows * pl.ns * D;
+    int rc = launch_fwd_kernel<D, BN, NW, CAUSAL, false, true>(
+        (unsigned)pl.grid, stream, "fa_fwd key-split kernel launch", static_cast<const _Float16*>(q),
+        static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk,
+        BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
+    if (rc != FA_OK) return rc;
     constexpr int R = fa::MergeCfg<D>::ROWS;
     hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
                        ksp.ws_o, ksp.ws_lse, static_cast<_Float16*>(o), lse, Sq, Cfg::BM, pl.ts, nsplit, pl.ns,
                        (int)rows);
-    rc = launched("fa_fwd key-split merge launch");
+    return launched("fa_fwd key-split merge launch");
   }
-  return rc;
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
                float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
   using Cfg = fa::FwdCfg<D, BN, NW>;
-  if (pl.ns > 1) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
+  if (pl.grid > 0) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   return launch_fwd_kernel<D, BN, NW, CAUSAL, false, false>(
       (unsigned)(nqt * BH), stream, "fa_fwd kernel launch", static_cast<const _Float16*>(q),
@@ -597,7 +724,7 @@ enum FwdKind { kFwdTile = 0, kFwdSplitD = 1, kFwdDecode = 2 };
 struct FwdPlan {
   int kind = kFwdTile;
   int nw = 4;     // wavefronts per workgroup of the tile kernel
-  SplitPlan sp;   // key split of the tile kernel (sp.ns > 1: split)
+  SplitPlan sp;   // even split of the tile kernel (sp.grid > 0: split)
   int ns = 1;     // key parts of Split-D, or decode partitions
   size_t ws = 0;  // workspace bytes (0: none)
 };
@@ -636,8 +763,11 @@ int compute_plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, 
     const int64_t nqt = (Sq + BM - 1) / BM;
     if (nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
     // small grids: the heaviest causal tiles, or too few tiles, leave CUs idle
-    if (p.nw == 4) p.sp = plan_fwd_split((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus);
-    if (p.sp.ns > 1) p.ws = ws_bytes(BH * (nqt - p.sp.ts) * BM, D, p.sp.ns);
+    if (p.nw == 4)
+      p.sp = D == 256 ? plan_fwd_runs((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus)
+                      : plan_fwd_parts((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus);
+    if (p.sp.grid > 0)
+      p.ws = D == 256 ? runs_ws_bytes(BM, D, p.sp) : ws_bytes(BH * (nqt - p.sp.ts) * BM, D, p.sp.ns);
   }
   *out = p;
   return FA_OK;
@@ -871,7 +1001,7 @@ int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_c
   if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return 0;
   FwdPlan p;
   if (plan_fwd(B, H, Sq, Sk, D, causal != 0, num_cus, &p) != FA_OK) return 0;
-  return p.kind == kFwdTile ? p.sp.ns : p.ns;
+  return p.kind == kFwdTile ? p.sp.max_parts : p.ns;
 }
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {

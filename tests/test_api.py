@@ -153,12 +153,12 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
     (8, 16, 2048, 2048, 32, 1, 256, 1),    # D = 32 (always 128-row workgroups): 2048 tiles
     (1, 8, 2048, 2048, 128, 0, 256, 1),    # D <= 128 non-causal: measured no gain, never split
     (2, 8, 1024, 1024, 128, 1, 256, 1),    # short tiles: the merge costs what the balance saves
-    (1, 16, 2048, 2048, 256, 1, 256, 1),   # 256 tiles, one per CU: the merge would cost about what it saves
+    (1, 16, 2048, 2048, 256, 1, 256, 2),   # D = 256 runs, one per CU: every heavy tile cut once
     (1, 16, 2048, 2048, 256, 0, 256, 1),   # full key range everywhere: every CU equally loaded
-    (1, 16, 1024, 1024, 256, 1, 256, 2),   # 128 tiles on 256 CUs
-    (1, 8, 4096, 4096, 256, 1, 256, 2),    # heaviest tiles twice the mean
-    (1, 4, 2048, 2048, 256, 0, 256, 3),    # 64 tiles on 256 CUs
-    (1, 2, 1000, 1000, 256, 1, 256, 4),
+    (1, 16, 1024, 1024, 256, 1, 256, 1),   # 128 short tiles: the merge would cost more than it saves
+    (1, 8, 4096, 4096, 256, 1, 256, 2),    # heaviest tiles twice the mean: every heavy tile cut once
+    (1, 4, 2048, 2048, 256, 0, 256, 4),    # 64 tiles on 256 CUs: four runs each
+    (1, 2, 1000, 1000, 256, 1, 256, 8),    # 16 tiles on 256 CUs: runs of 5 key tiles
     (8, 32, 2048, 2048, 256, 1, 256, 1),   # 4096 tiles: more than two per CU, never split
     (1, 4, 512, 512, 1024, 0, 256, 4),     # Split-D: 64 work items -> 4 parts
     (1, 8, 1024, 1024, 512, 0, 256, 1),    # Split-D: 256 work items fill the CUs
@@ -272,6 +272,9 @@ def test_fwd_workspace_bytes(lib, B, H, Sq, Sk, D, causal, cus):
         assert ws == lib.fa_decode_workspace_bytes(B, H, D, ns) == rup256(B * H * ns * (D + 1) * 4)
     elif D >= 512:
         assert ws == rup256(B * H * Sq * ns * (D + 1) * 4)
+    elif D == 256:
+        # runs: partial O and log2-sum-exp slots for two segments of each of G runs
+        assert any(ws == rup256(g * 2 * 128 * D * 4) + rup256(g * 2 * 128 * 4) for g in range(1, 2 * cus + 9)), ws
     else:
         # rows of the split 128-row query tiles: a whole number of tiles per slice
         assert ws % 256 == 0 and ws > 0

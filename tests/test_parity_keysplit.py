@@ -1,15 +1,18 @@
 """GPU parity of the key-split prefill against the CPU fp64 oracle.
 
-fa_fwd splits the key range of the heaviest query tiles of a small grid
-(D = 256; causal D <= 128 grids of the 4-wavefront kernel) into parts and merges them with log-sum-exp weights (the split-KV
+fa_fwd splits the key ranges of a small grid's query tiles (the split-KV
 scheme of "Adaptive High-Performance Attention Kernels in CUDA", Split-K /
-Flash-Decoding, on prefill tiles).  Every shape here is checked to be one
-that fa_fwd_key_splits() splits on this device, so these tests run the
-split kernel and its merge; the bar is the one of every prefill: max |dO|
-<= 2e-3, max |dLSE| <= 1e-3.  Also covered: bitwise repeatability, split
-calls of different workspace sizes queued without a sync, split calls on two
-streams at once (each with its own pool workspace), and fa_fwd_ws with a
-caller workspace (bit-identical to fa_fwd; a short workspace is refused).
+Flash-Decoding, on prefill tiles) and merges the parts with log-sum-exp
+weights: at D <= 128 (causal grids of the 4-wavefront kernel) the heaviest
+query tiles in equal parts, at D = 256 the key tiles of all query tiles cut
+into one run per CU (a tile cut between runs is merged by a second kernel).
+Every shape here is checked to be one that fa_fwd_key_splits() splits on
+this device, so these tests run the split kernels and their merges; the bar
+is the one of every prefill: max |dO| <= 2e-3, max |dLSE| <= 1e-3.  Also
+covered: bitwise repeatability, split calls of different workspace sizes
+queued without a sync, split calls on two streams at once (each with its own
+pool workspace), and fa_fwd_ws with a caller workspace (bit-identical to
+fa_fwd; a short workspace is refused).
 """
 import math
 
@@ -75,12 +78,12 @@ def test_split_calls_of_different_sizes_queued(env):
 
 SPLIT = [
     # B, H, Sq, Sk, causal
-    (1, 16, 1024, 1024, True),
+    (1, 8, 1024, 1024, True),
     (1, 4, 2048, 2048, False),
     (1, 2, 1000, 1000, True),
-    (1, 3, 200, 333, False),
+    (1, 2, 500, 1500, False),   # more keys than queries
     (1, 1, 777, 1500, True),
-    (1, 2, 300, 100, True),     # more queries than keys
+    (1, 1, 3000, 1000, True),   # more queries than keys
     (2, 1, 129, 1000, False),   # a ragged query tile of one row
 ]
 
@@ -97,8 +100,8 @@ def test_split_prefill_matches_oracle(env, shape):
 
 
 def test_split_long_causal_sampled_rows(env):
-    # (1, 8, 4096, 4096): the split tiles are the last quarter; rows sampled
-    # across every tile, both ends of each split tile among them
+    # (1, 8, 4096, 4096): every heavy tile cut once between two runs; rows
+    # sampled across every tile, both ends of the 128-row tiles among them
     torch = env[0]
     host, dev_in, ns = inputs(env, 1, 8, 4096, 4096, True, seed=41)
     o, lse = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
@@ -111,9 +114,25 @@ def test_split_long_causal_sampled_rows(env):
     check(o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], O, L, f"long causal sampled rows ns={ns}")
 
 
+def test_split_d256_benchmark_shape_sampled_rows(env):
+    # (1, 16, 2048, 2048) causal, the D = 256 prefill workload: runs of ~34
+    # key tiles, each heavy tile cut once; rows sampled from every head at the
+    # ends of query tiles and at random
+    torch = env[0]
+    host, dev_in, ns = inputs(env, 1, 16, 2048, 2048, True, seed=42)
+    o, lse = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = [(0, h, i) for h in range(16) for i in (0, 127, 128, 1023, 1024, 1919, 1920, 2047)]
+    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, 16, 64), rng.integers(0, 2048, 64))]
+    O, L = oracle.attention_rows(*host, True, 1 / 16, rows)
+    idx = tuple(np.array(rows).T)
+    check(o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], O, L, f"d256 benchmark shape sampled rows ns={ns}")
+
+
 def test_split_run_to_run_bitwise(env):
     torch = env[0]
-    _, dev_in, _ = inputs(env, 1, 16, 1024, 1024, True, seed=51)
+    _, dev_in, _ = inputs(env, 1, 8, 1024, 1024, True, seed=51)
     a = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
     b = env[2].fa_fwd(*dev_in, causal=True, scale=1 / 16)
     torch.cuda.synchronize()
@@ -125,7 +144,7 @@ def test_split_calls_on_two_streams(env):
     # call's workspace comes from the pool on its own stream, so the two
     # streams run concurrently without sharing a buffer
     torch, dev, fa, _ = env
-    shapes = [(1, 2, 1000, 1000, True), (1, 3, 200, 333, False)]
+    shapes = [(1, 2, 1000, 1000, True), (2, 1, 129, 1000, False)]
     cases = [inputs(env, B, H, Sq, Sk, c, seed=60 + i) + (c,) for i, (B, H, Sq, Sk, c) in enumerate(shapes)]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]  # default priority
@@ -185,8 +204,8 @@ def test_fwd_ws_caller_workspace_matches_fwd(env):
     # bit-identical to fa_fwd (same plan, same kernels); one byte short is
     # refused before any launch
     torch, dev, fa, cus = env
-    host, dev_in, ns = inputs(env, 1, 16, 1024, 1024, True, seed=71)
-    nbytes = fa.fa_fwd_workspace_bytes(1, 16, 1024, 1024, D, True, cus)
+    host, dev_in, ns = inputs(env, 1, 8, 1024, 1024, True, seed=71)
+    nbytes = fa.fa_fwd_workspace_bytes(1, 8, 1024, 1024, D, True, cus)
     assert nbytes > 0
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     a = fa.fa_fwd(*dev_in, causal=True, scale=1 / 16)
