@@ -469,8 +469,13 @@ def main():
     o5 = torch.empty_like(q5)
     l5 = torch.empty((w5.B, w5.H, w5.Sq), dtype=torch.float32, device=dev)
 
+    # split grids take a workspace: allocated once, as a serving loop would
+    # (fa_fwd_ws; fa_fwd would take it from the stream-ordered pool per call)
+    ws5_bytes = fa.fa_fwd_workspace_bytes(w5.B, w5.H, w5.Sq, w5.Sk, w5.D, True, cus)
+    ws5 = torch.empty(ws5_bytes, dtype=torch.uint8, device=dev) if ws5_bytes else None
+
     def d256():
-        fa.fa_fwd(q5, k5, v5, o5, l5, causal=True, scale=w5.scale)
+        fa.fa_fwd_ws(q5, k5, v5, ws5, o5, l5, causal=True, scale=w5.scale)
 
     for _ in range(args.warmup):
         d256()
@@ -510,8 +515,11 @@ def main():
     os_ = torch.empty_like(qs_)
     ls_ = torch.empty((1, hs, w3.Sq), dtype=torch.float32, device=dev)
 
+    wss_bytes = fa.fa_fwd_workspace_bytes(1, hs, w3.Sq, w3.Sk, w3.D, True, cus)
+    wss = torch.empty(wss_bytes, dtype=torch.uint8, device=dev) if wss_bytes else None
+
     def shard():
-        fa.fa_fwd(qs_, ks_, vs_, os_, ls_, causal=True, scale=w3.scale)
+        fa.fa_fwd_ws(qs_, ks_, vs_, wss, os_, ls_, causal=True, scale=w3.scale)
 
     for _ in range(args.warmup):
         shard()
@@ -546,8 +554,12 @@ def main():
         ox = torch.empty_like(qx)
         lx = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
         for causal in (False, True):
+            # key parts need a workspace: allocated once (fa_fwd_ws)
+            wsx_bytes = fa.fa_fwd_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, causal, cus)
+            wsx = torch.empty(wsx_bytes, dtype=torch.uint8, device=dev) if wsx_bytes else None
+
             def large_head():
-                fa.fa_fwd(qx, kx, vx, ox, lx, causal=causal, scale=w.scale)
+                fa.fa_fwd_ws(qx, kx, vx, wsx, ox, lx, causal=causal, scale=w.scale)
 
             for _ in range(args.warmup):
                 large_head()
@@ -632,6 +644,7 @@ def main():
             "d256_prefill_tflops": round(tflops_d256, 3),
             "d256_prefill_frac_of_peak": round(tflops_d256 / PEAK_FP16_TFLOPS, 4),
             "d256_prefill_us": round(t_d256 * 1e6, 2),
+            "d256_key_parts": fa.fa_fwd_key_splits(w5.B, w5.H, w5.Sq, w5.Sk, w5.D, True, cus),
             "head_shard_prefill_tflops": round(tflops_shard, 3),
             "head_shard_prefill_frac_of_peak": round(tflops_shard / PEAK_FP16_TFLOPS, 4),
             "head_shard_prefill_us": round(t_shard * 1e6, 2),
