@@ -86,10 +86,12 @@ enum fa_status {
  * (query tile, slice) work items are fewer than the CUs, the Split-D key
  * range is also split and the parts merged with log-sum-exp weights
  * ("Split-KV" of the same list).  A grid of at most two query tiles per CU
- * (D = 256; causal grids at D <= 128 too small for 256-row workgroups)
- * whose heaviest query tiles would leave most CUs idle near the end has the
- * key ranges of those tiles split, when fa_fwd_key_splits() says it pays; a
- * second kernel merges the parts.  Split calls keep their fp32 partials in
+ * whose heaviest query tiles would leave most CUs idle near the end has key
+ * ranges split, when fa_fwd_key_splits() says it pays: causal grids at D <=
+ * 128 too small for 256-row workgroups split the key ranges of their
+ * heaviest tiles into equal parts; at D = 256 the key tiles of all query
+ * tiles are cut into one run per CU (a tile cut between runs is processed
+ * in parts).  A second kernel merges the parts.  Split calls keep their fp32 partials in
  * a workspace of fa_fwd_workspace_bytes() bytes taken from the per-device
  * stream-ordered pool (hipMallocFromPoolAsync before the kernels,
  * hipFreeAsync after them, both on `stream`), so nothing blocks and calls on
@@ -112,8 +114,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * step with one partition); otherwise the fp32 partial outputs and LSEs of
  * the key parts, rows * parts * (D + 1) * 4 bytes rounded up to 256, where
  * rows are the query rows of the split tiles (B * H * Sq for Split-D, and
- * B * H for a decode step).  Pure host arithmetic; returns 0 for invalid
- * sizes too.
+ * B * H for a decode step); at D = 256, two 128-row slots of partial O and
+ * LSE per run, each of the two arrays rounded up to 256.  Pure host
+ * arithmetic; returns 0 for invalid sizes too.
  */
 size_t fa_fwd_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
 
@@ -291,19 +294,21 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus);
 
 /*
- * fa_fwd_key_splits -- the number of key-range parts that fa_fwd gives the
- * heaviest query tiles of these sizes on a device with num_cus CUs (1: no
- * split), the same choice fa_fwd makes ("Adaptive High-Performance
- * Attention Kernels in CUDA", Split-K / Flash-Decoding, applied to prefill
- * query tiles).  D = 256, and causal D = 32, 64, 128 grids of 128-row
- * workgroups (those with fewer 256-row tiles than CUs): chosen by
- * simulating the dispatch of the work items (heaviest first, each to the
- * CU that frees first) against the cost of merging the parts, with timing
- * constants measured per kernel; at most 8 parts.  Other D = 64, 128 grids:
- * 1.  D = 512, 1024: the Split-D key split (enough parts to give every CU a
- * work item when there are fewer than CUs, at most 16).  A decode step
- * (Sq = 1, causal = 0, D <= 256): the partitions of fa_decode_auto_splits.
- * Pure host arithmetic; returns 0 for invalid sizes.
+ * fa_fwd_key_splits -- the most key-range parts into which fa_fwd cuts any
+ * query tile of these sizes on a device with num_cus CUs (1: no split), the
+ * same plan fa_fwd makes ("Adaptive High-Performance Attention Kernels in
+ * CUDA", Split-K / Flash-Decoding, applied to prefill query tiles).  Causal
+ * D = 32, 64, 128 grids of 128-row workgroups (those with fewer 256-row
+ * tiles than CUs): the parts of the heaviest tiles, chosen by simulating
+ * the dispatch of the work items (heaviest first, each to the CU that frees
+ * first) against the cost of merging the parts.  D = 256 grids of at most
+ * two query tiles per CU: one run of key tiles per CU, chosen by modelling
+ * each run's segments against the unsplit grid and the merge.  Timing
+ * constants are measured per kernel; at most 8 parts.  Other D = 64, 128
+ * grids: 1.  D = 512, 1024: the Split-D key split (enough parts to give
+ * every CU a work item when there are fewer than CUs, at most 16).  A
+ * decode step (Sq = 1, causal = 0, D <= 256): the partitions of
+ * fa_decode_auto_splits.  Pure host arithmetic; returns 0 for invalid sizes.
  */
 int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus);
 
