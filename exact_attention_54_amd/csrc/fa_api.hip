@@ -293,11 +293,11 @@ size_t runs_ws_bytes(int BM, int D, const SplitPlan& pl) {
 }
 
 // Launches an instantiation of fa::fwd_kernel (its LDS is static).
-template <int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool KSPLIT, class... Args>
+template <int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool KSPLIT, int RES = 0, class... Args>
 int launch_fwd_kernel(unsigned grid, hipStream_t stream, const char* what, Args... args) {
   using Cfg = fa::FwdCfg<D, BN, NW>;
-  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, VARLEN, KSPLIT>), dim3(grid), dim3(Cfg::THREADS), 0, stream,
-                     args...);
+  hipLaunchKernelGGL((fa::fwd_kernel<D, BN, NW, CAUSAL, VARLEN, KSPLIT, RES>), dim3(grid), dim3(Cfg::THREADS), 0,
+                     stream, args...);
   return launched(what);
 }
 
@@ -355,10 +355,19 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   using Cfg = fa::FwdCfg<D, BN, NW>;
   if (pl.grid > 0) return launch_fwd_split<D, BN, NW, CAUSAL>(q, k, v, o, lse, BH, Sq, Sk, scale, stream, pl, ws);
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
-  return launch_fwd_kernel<D, BN, NW, CAUSAL, false, false>(
-      (unsigned)(nqt * BH), stream, "fa_fwd kernel launch", static_cast<const _Float16*>(q),
-      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH,
-      nqt, scale * fa::kLog2e, fa::VarlenArgs{}, fa::KeySplit{});
+  auto run = [&](auto res) {
+    return launch_fwd_kernel<D, BN, NW, CAUSAL, false, false, decltype(res)::value>(
+        (unsigned)(nqt * BH), stream, "fa_fwd kernel launch", static_cast<const _Float16*>(q),
+        static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk, BH,
+        nqt, scale * fa::kLog2e, fa::VarlenArgs{}, fa::KeySplit{});
+  };
+  // short key ranges on the two-workgroups-per-CU kernel: every key tile
+  // copied to LDS once, in the prologue
+  if constexpr (NW == 4 && D <= 128) {
+    constexpr int RES = fa::fwd_resident_tiles<D, BN>();
+    if ((Sk + BN - 1) / BN <= RES) return run(std::integral_constant<int, RES>{});
+  }
+  return run(std::integral_constant<int, 0>{});
 }
 
 // The tile kernel of head dim D with the geometry the plan chose: D = 256

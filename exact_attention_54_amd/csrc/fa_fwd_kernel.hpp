@@ -77,6 +77,16 @@ struct FwdCfg {
 template <int D, int NW>
 constexpr int fwd_wg_per_cu() { return (D <= 128 && NW == 4) ? 2 : 1; }
 
+// Resident key tiles (fwd_kernel RES > 0): LDS for RES K and RES V tiles,
+// or the epilogue's transpose if larger; and the largest RES whose tiles fit
+// the 64 KiB of static LDS.
+template <int D, int BN, int NW, int RES>
+constexpr int fwd_resident_lds() {
+  return (2 * RES * BN * D * 2 > NW * 32 * D * 2) ? 2 * RES * BN * D * 2 : NW * 32 * D * 2;
+}
+template <int D, int BN>
+constexpr int fwd_resident_tiles() { return 65536 / (2 * BN * D * 2); }
+
 // Packed variable-length batches ("Adaptive High-Performance Attention
 // Kernels in CUDA", Advanced Production Features, 3. Ragged / Variable-Length
 // Sequences): tokens of all sequences in one stream [total, H, D], sequence
@@ -161,13 +171,19 @@ __host__ __device__ inline int split_position(int rank, int nqt) {
   return (2 * rank < nqt) ? 2 * rank : 2 * (nqt - 1 - rank) + 1;
 }
 
-template <int D, int BN, int NW, bool CAUSAL, bool VARLEN = false, bool KSPLIT = false>
+template <int D, int BN, int NW, bool CAUSAL, bool VARLEN = false, bool KSPLIT = false, int RES = 0>
 __global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<D, NW>()))
 fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
            const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
            int Sq, int Sk, int BH, int nqt, float c2, VarlenArgs va = {}, KeySplit ksp = {}) {
   using C = FwdCfg<D, BN, NW>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // RES > 0: every key tile of the slice (at most RES) is copied to LDS
+  // in the prologue and stays, so the loop waits for no copy (short key
+  // ranges, where each streamed tile would cost a memory round trip)
+  constexpr bool RESIDENT = RES > 0;
+  static_assert(!RESIDENT || (!VARLEN && !KSPLIT), "resident tiles: dense, unsplit grids");
+  constexpr int LDS_BYTES = RESIDENT ? fwd_resident_lds<D, BN, NW, RES>() : C::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -337,6 +353,10 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
     const u32x4 rkw = rsrc_words(ks_, extent(Sk));
     const u32x4 rvw = rsrc_words(vs, extent(Sk));
     const uint32_t lds0 = lds_addr_of(smem);
+  // LDS slot of key tile kt: two-stage rings (K0 K1 V0 V1), or one slot per
+  // tile (K0..K(RES-1) V0..V(RES-1)) for resident tiles
+  constexpr int V_BASE = RESIDENT ? RES * C::TILE_BYTES : C::V_BASE;
+  auto kst = [](int kt) { return RESIDENT ? kt : (kt & 1); };
     auto load_k = [&](int kt, int stage) {
       const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
@@ -347,7 +367,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       const uint32_t tb = (uint32_t)kt * tile_stride;
 #pragma unroll
       for (int u = 0; u < C::LPW; ++u)
-        dma16(rvw, lds0 + C::V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
+        dma16(rvw, lds0 + V_BASE + stage * C::TILE_BYTES + (w * C::LPW + u) * 1024, tb + vgo[u]);
     };
 
     // S^T = K Q^T for the tile in K stage `stage`.
@@ -449,11 +469,11 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       constexpr bool NEXT = decltype(next_tag)::value;
       h8 pop[C::NKB][2];
       float t = softmax_tile(s_c, pop);
-      if constexpr (NEXT) qk((kt + 1) & 1, s_n);
+      if constexpr (NEXT) qk(kst(kt + 1), s_n);
       refit(s_c, pop, t);
       l_run += t;
 
-      const char* Vs = smem + C::V_BASE + (kt & 1) * C::TILE_BYTES;
+      const char* Vs = smem + V_BASE + kst(kt) * C::TILE_BYTES;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -473,14 +493,21 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
 
     // Prologue: K(kb), V(kb), K(kb+1) resident, S(kb) computed, masked and maxed.
     if (!KSPLIT || kb < ke) {
-      load_k(kb, kb & 1);
-      load_v(kb, kb & 1);
+      load_k(kb, kst(kb));
+      load_v(kb, kst(kb));
     }
-    if (kb + 1 < ke) load_k(kb + 1, (kb + 1) & 1);
+    if constexpr (RESIDENT) {
+      for (int t = kb + 1; t < ke; ++t) {
+        load_k(t, t);
+        load_v(t, t);
+      }
+    } else if (kb + 1 < ke) {
+      load_k(kb + 1, kst(kb + 1));
+    }
     wait_vmem_all();
     __syncthreads();
     if (jlast >= kb) {
-      qk(kb & 1, s_cur);
+      qk(kst(kb), s_cur);
       if (tile_needs_mask(kb)) mask_tile(s_cur, kb);
       // the reference starts at the first tile's row max (a row without a
       // visible key there keeps kMRunInit), so its P needs no refit
@@ -491,15 +518,19 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
         for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, s_cur[kb2][j]), s_cur[kb2][j + 1]);
       m_run = fmaxf(xhalf_max(mx) * c2, kMRunInit);
     }
-    __syncthreads();  // K stage 0 is refilled with K(2) below
+    if constexpr (!RESIDENT) __syncthreads();  // K stage 0 is refilled with K(2) below
 
     auto begin_tile = [&](int kt) {
-      if (kt + 2 < ke) load_k(kt + 2, kt & 1);
-      if (kt + 1 < ke) load_v(kt + 1, (kt + 1) & 1);
+      if constexpr (!RESIDENT) {
+        if (kt + 2 < ke) load_k(kt + 2, kst(kt + 2));
+        if (kt + 1 < ke) load_v(kt + 1, kst(kt + 1));
+      }
     };
     auto end_tile = [&]() {
-      wait_vmem_all();
-      __syncthreads();
+      if constexpr (!RESIDENT) {
+        wait_vmem_all();
+        __syncthreads();
+      }
     };
 
     // Hot loop, unrolled by two so the current / next S^T register sets swap
@@ -580,6 +611,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       }
       continue;  // the last step's barrier already ended every LDS read
     }
+    if constexpr (RESIDENT) __syncthreads();  // every wavefront is done reading K / V
     char* Os = smem + w * (32 * D * 2);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
