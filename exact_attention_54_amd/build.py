@@ -6,8 +6,10 @@ Produces ``exact_attention_54_amd/libfa_hip.so`` from ``csrc/fa_api.hip``
 (the C ABI of ``include/fa.h`` plus every kernel), the streaming-read /
 MFMA loop probes ``exact_attention_54_amd/libroofline_probe.so`` from
 ``csrc/roofline_probe.hip`` that bench.py reports as context, the test-only
-MFMA layout probe ``tests/hip/libmfma_probe.so`` and the host-side LDS
-layout check ``tests/hip/libswizzle_check.so``.  Always recompiles.
+MFMA layout probe ``tests/hip/libmfma_probe.so``, and the host-side checks
+of the LDS layouts ``tests/hip/libswizzle_check.so`` and of the split
+prefill's index arithmetic ``tests/hip/libsplit_check.so``.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -134,9 +136,18 @@ def build_swizzle_check(verbose: bool = False) -> str:
     return compile_shared([SWIZZLE_SRC], SWIZZLE_LIB, include_dirs=[CSRC], verbose=verbose)
 
 
+SPLIT_SRC = os.path.join(ROOT, "tests", "hip", "split_check.hip")
+SPLIT_LIB = os.path.join(ROOT, "tests", "hip", "libsplit_check.so")
+
+
+def build_split_check(verbose: bool = False) -> str:
+    """Host-side check of the split prefill's index arithmetic, used by tests/test_split_index.py."""
+    return compile_shared([SPLIT_SRC], SPLIT_LIB, include_dirs=[CSRC], verbose=verbose)
+
+
 def build_all(verbose: bool = False):
     return [build_library(verbose), build_test_probe(verbose), build_roofline_probe(verbose),
-            build_swizzle_check(verbose)]
+            build_swizzle_check(verbose), build_split_check(verbose)]
 
 
 if __name__ == "__main__":

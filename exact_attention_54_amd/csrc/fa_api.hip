@@ -102,7 +102,7 @@ size_t ws_bytes(int64_t BH, int D, int ns);
 // tiles of all query tiles cut into `grid` runs (split_start).
 struct SplitPlan {
   int ts = 0, ns = 1;     // parts
-  int chunk = 0, bias = 0;  // runs
+  int runs = 0, bias = 0;  // runs: run count and bias (split_start)
   int units = 0;          // runs: key tiles of one slice
   int64_t total = 0;      // runs: key tiles of all slices
   int64_t grid = 0;       // workgroups of the split kernel (0: no split)
@@ -203,6 +203,15 @@ struct RunsModel {
 
 constexpr RunsModel kRunsModel = {0.82, 6.0, 0.92, 7.9, 3.9, 3.0, 4.0e6};
 
+// The same model for the Split-D kernel at D = 512 (32-row tiles, 32-key
+// tiles): unsplit, 50.6 us for the heaviest causal tile (32 key tiles) run
+// while the others finish; split into runs of 16.5 key tiles, 35.9 us plus
+// an 8.6 us merge of 16 MiB of partials (kernel trace, (1, 8, 1024, 1024,
+// 512) causal).  At D = 1024 the grids of the pages' shapes are too short
+// for runs (544 key tiles on 256 CUs): runs measured slower than equal key
+// parts there, so D = 1024 keeps the parts.
+constexpr RunsModel kSplitDRunsModel = {1.46, 4.0, 1.69, 5.0, 3.0, 4.5, 4.0e6};
+
 // Makespan of the unsplit grid: query tiles heaviest first, each to the CU
 // that frees first.
 double fwd_unsplit_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool causal, int cus, const RunsModel& m) {
@@ -221,10 +230,10 @@ double fwd_unsplit_time(int nqt, int BH, int BM, int BN, int Sq, int Sk, bool ca
 
 // Modelled time of these runs: the slowest run, plus the merge of the cut
 // tiles.  Also reports the most parts of any tile.
-double fwd_runs_time(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int chunk, int bias,
-                     int64_t grid, const RunsModel& m, int* max_parts) {
-  std::vector<double> cost((size_t)grid, 0.0);
-  std::vector<char> started((size_t)grid, 0);
+double fwd_runs_time(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int runs, int total,
+                     int bias, const RunsModel& m, int* max_parts) {
+  std::vector<double> cost((size_t)runs, 0.0);
+  std::vector<char> started((size_t)runs, 0);
   int64_t cut_parts = 0;
   *max_parts = 1;
   int64_t lin = 0;
@@ -232,10 +241,11 @@ double fwd_runs_time(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, boo
     for (int i = 0; i < nqt; ++i) {
       const int r = fa::split_order(i, nqt);
       const int u = fa::fwd_tile_units(causal ? nqt - 1 - r : r, BM, BN, Sq, Sk, causal);
-      const int g0 = fa::split_run((int)lin, chunk, bias), g1 = fa::split_run((int)(lin + u - 1), chunk, bias);
+      const int g0 = fa::split_run((int)lin, runs, total, bias);
+      const int g1 = fa::split_run((int)(lin + u - 1), runs, total, bias);
       for (int g = g0; g <= g1; ++g) {
-        const int64_t lo = std::max<int64_t>(lin, fa::split_start(g, chunk, bias));
-        const int64_t hi = std::min<int64_t>(lin + u, fa::split_start(g + 1, chunk, bias));
+        const int64_t lo = std::max<int64_t>(lin, fa::split_start(g, runs, total, bias));
+        const int64_t hi = std::min<int64_t>(lin + u, fa::split_start(g + 1, runs, total, bias));
         cost[(size_t)g] += (hi - lo) * m.unit_us + (started[(size_t)g] ? m.seg_us : m.first_us);
         started[(size_t)g] = 1;
       }
@@ -248,36 +258,41 @@ double fwd_runs_time(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, boo
 }
 
 // Split only grids of at most two query tiles per CU, and only when the
-// best modelled runs (one per CU, biases 0 .. chunk / 4) beat the unsplit
-// grid by 10%.
-SplitPlan plan_fwd_runs(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus) {
+// best modelled runs (one per CU, biases 0 .. a quarter of a run) beat the
+// unsplit grid by 10%.
+SplitPlan plan_fwd_runs(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, bool causal, int cus,
+                        const RunsModel& m) {
   SplitPlan best;
-  const RunsModel& m = kRunsModel;
   if (cus < 1 || (int64_t)nqt * BH > 2 * (int64_t)cus) return best;
   int64_t units = 0;
-  for (int t = 0; t < nqt; ++t) units += fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal);
+  int umax = 0;
+  for (int t = 0; t < nqt; ++t) {
+    const int u = fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal);
+    units += u;
+    umax = std::max(umax, u);
+  }
   const int64_t total = units * BH;
   if (total > (int64_t)1 << 28) return best;
   double best_time = 0.9 * fwd_unsplit_time(nqt, BH, BM, BN, Sq, Sk, causal, cus, m);
-  // at least 4 key tiles per run, and no tile in more than 8 parts (what
-  // the merge loads at once): a run holds at least a seventh of the longest
-  // tile
-  int umax = 0;
-  for (int t = 0; t < nqt; ++t) umax = std::max(umax, fa::fwd_tile_units(t, BM, BN, Sq, Sk, causal));
-  const int64_t chunk = std::max<int64_t>(std::max(4, (umax + 6) / 7), (total + cus - 1) / cus);
-  const int step = std::max<int>(1, (int)(chunk / 4) / 8);
-  for (int bias = 0; bias <= chunk / 4; bias += step) {
-    int64_t grid = (total + chunk - 1) / chunk;
-    while (fa::split_start((int)grid, (int)chunk, bias) < total) ++grid;
+  // one run per CU, but at least 4 key tiles per run, and no tile in more
+  // than 8 parts (what the merge loads at once): a run holds at least a
+  // seventh of the longest tile
+  int64_t runs = std::min<int64_t>(cus, total / 4);
+  runs = std::min<int64_t>(runs, 7 * total / umax);
+  if (runs < 2) return best;
+  const int len = (int)(total / runs);  // shortest run before the bias
+  const int step = std::max(1, (len / 4) / 8);
+  for (int bias = 0; bias <= len / 4; bias += step) {
     int max_parts = 1;
-    const double t = fwd_runs_time(nqt, BH, BM, BN, D, Sq, Sk, causal, (int)chunk, bias, grid, m, &max_parts);
+    const double t =
+        fwd_runs_time(nqt, BH, BM, BN, D, Sq, Sk, causal, (int)runs, (int)total, bias, m, &max_parts);
     if (t < best_time) {
       best_time = t;
-      best.chunk = (int)chunk;
+      best.runs = (int)runs;
       best.bias = bias;
       best.units = (int)units;
       best.total = total;
-      best.grid = grid;
+      best.grid = runs;
       best.max_parts = max_parts;
     }
   }
@@ -308,7 +323,7 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
   const int nqt = (Sq + Cfg::BM - 1) / Cfg::BM;
   fa::KeySplit ksp = {};
   if constexpr (fa::split_by_runs<D>()) {
-    ksp.chunk = pl.chunk;
+    ksp.runs = pl.runs;
     ksp.bias = pl.bias;
     ksp.units = pl.units;
     ksp.total = (int)pl.total;
@@ -624,9 +639,43 @@ int splitd_parts(int64_t work_items, int nkt_all, int cus) {
   return (int)std::max<int64_t>(ns, 1);
 }
 
+// Split-D split into runs (fwd_splitd_kernel<D, CAUSAL, true>) and the
+// merge of its cut tiles.
+template <int D, bool CAUSAL>
+int launch_fwd_splitd_runs(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
+                           float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
+  const int nqt = (Sq + 31) / 32;
+  fa::KeySplit ksp = {};
+  ksp.runs = pl.runs;
+  ksp.bias = pl.bias;
+  ksp.units = pl.units;
+  ksp.total = (int)pl.total;
+  ksp.ws_o = static_cast<float*>(ws);
+  ksp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)pl.grid * 2 * 32 * D * 4));
+  hipLaunchKernelGGL((fa::fwd_splitd_kernel<D, CAUSAL, true>), dim3((unsigned)((pl.grid + 7) / 8 * 8)),
+                     dim3(fa::SplitDCfg<D>::THREADS), 0, stream, static_cast<const _Float16*>(q),
+                     static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse,
+                     Sq, Sk, BH, nqt, 1, scale * fa::kLog2e, nullptr, nullptr, ksp);
+  int rc = launched("fa_fwd Split-D split kernel launch");
+  if (rc != FA_OK) return rc;
+  auto merge = [&](auto nparts) {
+    constexpr int NP = decltype(nparts)::value;
+    using M = fa::SplitMergeCfg<D, 32, NP>;
+    hipLaunchKernelGGL((fa::fwd_split_merge_kernel<D, 32, 32, CAUSAL, NP>), dim3((unsigned)(BH * nqt * M::BLOCKS)),
+                       dim3(M::THREADS), 0, stream, ksp, static_cast<_Float16*>(o), lse, Sq, Sk, nqt);
+    return launched("fa_fwd Split-D split merge launch");
+  };
+  if (pl.max_parts <= 2) return merge(std::integral_constant<int, 2>{});
+  if (pl.max_parts <= 4) return merge(std::integral_constant<int, 4>{});
+  return merge(std::integral_constant<int, 8>{});
+}
+
 template <int D>
 int run_fwd_splitd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
-                   int causal, float scale, hipStream_t s, int ns, void* ws) {
+                   int causal, float scale, hipStream_t s, int ns, void* ws, const SplitPlan& pl) {
+  if (pl.grid > 0)
+    return causal ? launch_fwd_splitd_runs<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, pl, ws)
+                  : launch_fwd_splitd_runs<D, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, pl, ws);
   float* ws_o = static_cast<float*>(ws);  // unused (may be null) without a key split
   float* ws_lse = ns > 1 ? ws_o + (size_t)BH * Sq * ns * D : nullptr;
   return causal ? launch_fwd_splitd<D, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, ns, ws_o, ws_lse)
@@ -756,8 +805,16 @@ int compute_plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, 
     p.kind = kFwdSplitD;
     const int64_t nqt = (Sq + 31) / 32;
     if (nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-    p.ns = splitd_parts(nqt * BH, (Sk + 31) / 32, cus);
-    p.ws = p.ns > 1 ? ws_bytes(BH * Sq, D, p.ns) : 0;
+    // runs of key tiles when the model says they pay (small or causal
+    // grids), else equal key parts when the grid is too small
+    if (D == 512) p.sp = plan_fwd_runs((int)nqt, (int)BH, 32, 32, D, Sq, Sk, causal, cus, kSplitDRunsModel);
+    if (p.sp.grid > 0) {
+      p.ns = 1;
+      p.ws = runs_ws_bytes(32, D, p.sp);
+    } else {
+      p.ns = splitd_parts(nqt * BH, (Sk + 31) / 32, cus);
+      p.ws = p.ns > 1 ? ws_bytes(BH * Sq, D, p.ns) : 0;
+    }
   } else {
     int BM = 128, BN = 64;
     if (D == 256) {
@@ -773,7 +830,7 @@ int compute_plan_fwd(int B, int H, int Sq, int Sk, int D, bool causal, int cus, 
     if (nqt * BH > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
     // small grids: the heaviest causal tiles, or too few tiles, leave CUs idle
     if (p.nw == 4)
-      p.sp = D == 256 ? plan_fwd_runs((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus)
+      p.sp = D == 256 ? plan_fwd_runs((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus, kRunsModel)
                       : plan_fwd_parts((int)nqt, (int)BH, BM, BN, D, Sq, Sk, causal, cus);
     if (p.sp.grid > 0)
       p.ws = D == 256 ? runs_ws_bytes(BM, D, p.sp) : ws_bytes(BH * (nqt - p.sp.ts) * BM, D, p.sp.ns);
@@ -845,9 +902,9 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
       return causal ? launch_fwd_d<256, true>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws)
                     : launch_fwd_d<256, false>(q, k, v, o, lse, BH, Sq, Sk, scale, s, p.nw, p.sp, ws);
     case 512:
-      return run_fwd_splitd<512>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws);
+      return run_fwd_splitd<512>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws, p.sp);
     default:
-      return run_fwd_splitd<1024>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws);
+      return run_fwd_splitd<1024>(q, k, v, o, lse, BH, Sq, Sk, causal, scale, s, p.ns, ws, p.sp);
   }
 }
 
@@ -1010,7 +1067,7 @@ int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_c
   if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return 0;
   FwdPlan p;
   if (plan_fwd(B, H, Sq, Sk, D, causal != 0, num_cus, &p) != FA_OK) return 0;
-  return p.kind == kFwdTile ? p.sp.max_parts : p.ns;
+  return (p.kind == kFwdTile || p.sp.grid > 0) ? p.sp.max_parts : p.ns;
 }
 
 int fa_decode_auto_splits(int B, int H, int Sk, int num_cus) {

@@ -117,7 +117,7 @@ struct VarlenArgs {
 // row of key tiles (its query tiles in split_order, each with the key tiles
 // it visits); the rows of all slices are laid end to end and cut into runs,
 // one per workgroup: run g starts at key-tile position split_start(g), i.e.
-// even runs get chunk + bias key tiles and odd runs chunk - bias (the bias
+// even runs get total / runs + bias key tiles and odd runs that - bias (the bias
 // leaves room for the second segment that an odd run of a causal grid
 // usually holds).  A run is a few segments (a query tile over a range of its
 // key tiles).  A segment that holds all of its tile's key tiles writes O and
@@ -126,8 +126,8 @@ struct VarlenArgs {
 // every cut tile in part order.
 struct KeySplit {
   int ts, ns;    // parts: first split query tile, parts per split tile
-  int chunk;     // runs: mean key tiles per run
-  int bias;      // runs: 0 <= bias < chunk
+  int runs;      // runs: number of runs (workgroups doing work)
+  int bias;      // runs: 0 <= bias < total / runs
   int units;     // runs: key tiles of one slice
   int total;     // runs: key tiles of all slices
   float* ws_o;   // parts: [BH * (nqt - ts) * BM, ns, D]; runs: [grid, 2, BM, D]
@@ -138,20 +138,25 @@ struct KeySplit {
 template <int D>
 constexpr bool split_by_runs() { return D == 256; }
 
-// First key-tile position of run g, and the run that holds position x.
-__host__ __device__ inline long long split_start(int g, int chunk, int bias) {
-  return (long long)g * chunk + ((g & 1) ? bias : 0);
+// First key-tile position of run g of `runs` over `total` key tiles (odd
+// runs start `bias` later), and the run that holds position x.  Runs are
+// floor(total / runs) or one more key tiles long before the bias, so two
+// consecutive runs cover exactly one (heavy, light) pair whenever the pairs
+// hold 2 * total / runs key tiles.
+__host__ __device__ inline long long split_start(int g, int runs, int total, int bias) {
+  return (long long)g * total / runs + ((g & 1) ? bias : 0);
 }
-__host__ __device__ inline int split_run(int x, int chunk, int bias) {
-  const int k = x / (2 * chunk);
-  return 2 * k + ((x - 2 * k * chunk) >= chunk + bias ? 1 : 0);
+__host__ __device__ inline int split_run(int x, int runs, int total, int bias) {
+  int g = (int)(((long long)(x + 1) * runs - 1) / total);
+  if ((g & 1) && split_start(g, runs, total, bias) > x) --g;
+  return g;
 }
 
 // Workspace slot of run g's segment of a tile that starts at key-tile
 // position tile_lin: a tile that began in an earlier run is its run's first
 // segment, else its last.
-__host__ __device__ inline size_t split_slot(int g, int tile_lin, int chunk, int bias) {
-  return (size_t)g * 2 + (tile_lin < split_start(g, chunk, bias) ? 0 : 1);
+__host__ __device__ inline size_t split_slot(int g, int tile_lin, int runs, int total, int bias) {
+  return (size_t)g * 2 + (tile_lin < split_start(g, runs, total, bias) ? 0 : 1);
 }
 
 // Key tiles of BN keys that query tile t (BM rows) visits.
@@ -243,8 +248,8 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
   int run = 0, lin = 0, lin_end = 0;
   if constexpr (RUNS) {
     run = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
-    lin = (int)min(split_start(run, ksp.chunk, ksp.bias), (long long)ksp.total);
-    lin_end = (int)min(split_start(run + 1, ksp.chunk, ksp.bias), (long long)ksp.total);
+    lin = (int)min(split_start(run, ksp.runs, ksp.total, ksp.bias), (long long)ksp.total);
+    lin_end = (int)min(split_start(run + 1, ksp.runs, ksp.total, ksp.bias), (long long)ksp.total);
   }
   for (;;) {
     int seg_kb = 0, seg_ke = 0, seg_units = 0, tile_lin = 0;
@@ -596,7 +601,7 @@ fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
       // a segment of a tile cut between runs: normalised fp32 partial O and
       // its log2-sum-exp for the merge kernel
       if (qi < Sq) {
-        const size_t slot = split_slot(run, tile_lin, ksp.chunk, ksp.bias);
+        const size_t slot = split_slot(run, tile_lin, ksp.runs, ksp.total, ksp.bias);
         float* po = ksp.ws_o + (slot * C::BM + (qi - q0)) * D;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
@@ -678,8 +683,8 @@ fwd_split_merge_kernel(KeySplit ksp, _Float16* __restrict__ O, float* __restrict
     const int r = split_order(i, nqt);
     tile_lin += fwd_tile_units(CAUSAL ? nqt - 1 - r : r, BM, BN, Sq, Sk, CAUSAL);
   }
-  const int g0 = split_run(tile_lin, ksp.chunk, ksp.bias);
-  const int g1 = split_run(tile_lin + u - 1, ksp.chunk, ksp.bias);
+  const int g0 = split_run(tile_lin, ksp.runs, ksp.total, ksp.bias);
+  const int g1 = split_run(tile_lin + u - 1, ksp.runs, ksp.total, ksp.bias);
   if (g0 == g1) return;  // written whole by its run
   const int d0 = 4 * ((int)threadIdx.x % M::TPR);
   const int r0 = rb + (int)threadIdx.x / M::TPR;
@@ -702,7 +707,7 @@ fwd_split_merge_kernel(KeySplit ksp, _Float16* __restrict__ O, float* __restrict
     float lp[M::PASSES][M::NP];
     f32x4 xp[M::PASSES][M::NP];
 #pragma unroll
-    for (int i = 0; i < M::NP; ++i) slot[i] = split_slot(min(g0 + i, g1), tile_lin, ksp.chunk, ksp.bias);
+    for (int i = 0; i < M::NP; ++i) slot[i] = split_slot(min(g0 + i, g1), tile_lin, ksp.runs, ksp.total, ksp.bias);
 #pragma unroll
     for (int k = 0; k < M::PASSES; ++k)
 #pragma unroll
@@ -739,12 +744,12 @@ fwd_split_merge_kernel(KeySplit ksp, _Float16* __restrict__ O, float* __restrict
   for (int k = 0; k < M::PASSES; ++k) {
     const int rrow = r0 + k * M::RPP;
     float mx = kNegInf;
-    for (int p = g0; p <= g1; ++p) mx = fmaxf(mx, ksp.ws_lse[split_slot(p, tile_lin, ksp.chunk, ksp.bias) * BM + rrow]);
+    for (int p = g0; p <= g1; ++p) mx = fmaxf(mx, ksp.ws_lse[split_slot(p, tile_lin, ksp.runs, ksp.total, ksp.bias) * BM + rrow]);
     float den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     if (mx != kNegInf) {
       for (int p = g0; p <= g1; ++p) {
-        const size_t row = split_slot(p, tile_lin, ksp.chunk, ksp.bias) * BM + rrow;
+        const size_t row = split_slot(p, tile_lin, ksp.runs, ksp.total, ksp.bias) * BM + rrow;
         const float wgt = exp2_fast(ksp.ws_lse[row] - mx);
         const f32x4 x = *reinterpret_cast<const f32x4*>(ksp.ws_o + row * D + d0);
         den += wgt;

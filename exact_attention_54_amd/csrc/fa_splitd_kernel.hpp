@@ -26,6 +26,7 @@
 #pragma once
 
 #include "fa_device.hpp"
+#include "fa_fwd_kernel.hpp"
 
 namespace fa {
 
@@ -55,12 +56,17 @@ struct SplitDCfg {
 // partition the tile for the reduce-scatter into contiguous pieces.
 __device__ __forceinline__ int red_off(int L, int j) { return (j >> 2) * 256 + L * 4 + (j & 3); }
 
-template <int D, bool CAUSAL>
+// RUNS: the grid is split into runs of key tiles, as fwd_kernel does for
+// D = 256 (KeySplit, fa_fwd_kernel.hpp): 32-row query tiles in split_order,
+// one run per workgroup, each run a few segments, cut tiles written as fp32
+// partials for fwd_split_merge_kernel.  Otherwise work item = key part s of
+// a query tile (ns parts of equal length, merged by fwd_merge_kernel).
+template <int D, bool CAUSAL, bool RUNS = false>
 __global__ void __launch_bounds__(64 * (D / 128), 1)
 fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                   const _Float16* __restrict__ V, _Float16* __restrict__ O, float* __restrict__ LSE,
                   int Sq, int Sk, int BH, int nqt, int ns, float c2, float* __restrict__ ws_o,
-                  float* __restrict__ ws_lse) {
+                  float* __restrict__ ws_lse, KeySplit ksp = {}) {
   using C = SplitDCfg<D>;
   constexpr int NW = C::NW;
   __shared__ __attribute__((aligned(1024))) char smem[C::BYTES];
@@ -71,11 +77,36 @@ fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K
   const int r32 = lane & 31;
   const int hh = lane >> 5;
 
-  // work item: key part s of query-tile rank `rank` of slice bh
-  const int s = (int)(blockIdx.x % (unsigned)ns);
-  const int rest = (int)(blockIdx.x / (unsigned)ns);
-  const int rank = rest / BH;
-  const int bh = rest - rank * BH;
+  // parts: key part s of query-tile rank `rank` of slice bh
+  int s = (int)(blockIdx.x % (unsigned)ns);
+  int rank = (int)(blockIdx.x / (unsigned)ns) / BH;
+  int bh = (int)(blockIdx.x / (unsigned)ns) - rank * BH;
+  // runs: this workgroup's run (XCD-local, as in fwd_kernel)
+  int run = 0, lin = 0, lin_end = 0;
+  if constexpr (RUNS) {
+    run = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    lin = (int)min(split_start(run, ksp.runs, ksp.total, ksp.bias), (long long)ksp.total);
+    lin_end = (int)min(split_start(run + 1, ksp.runs, ksp.total, ksp.bias), (long long)ksp.total);
+  }
+  for (;;) {
+  int seg_kb = 0, seg_ke = 0, seg_units = 0, tile_lin = 0;
+  if constexpr (RUNS) {
+    if (lin >= lin_end) return;
+    bh = lin / ksp.units;
+    const int off = lin - bh * ksp.units;
+    int base = 0;
+    for (int i = 0;; ++i) {
+      rank = split_order(i, nqt);
+      seg_units = fwd_tile_units(CAUSAL ? nqt - 1 - rank : rank, 32, C::BN, Sq, Sk, CAUSAL);
+      if (off < base + seg_units || i == nqt - 1) break;
+      base += seg_units;
+    }
+    seg_kb = off - base;
+    seg_ke = min(seg_units, seg_kb + (lin_end - lin));
+    tile_lin = lin - seg_kb;
+    lin += seg_ke - seg_kb;
+    s = 0;
+  }
   const int qt = CAUSAL ? (nqt - 1 - rank) : rank;  // heaviest first
   const int q0 = qt * 32;
   const int qi = q0 + r32;
@@ -92,8 +123,9 @@ fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K
 
   const int nkt_all = (Sk + C::BN - 1) / C::BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + 32, Sk) + C::BN - 1) / C::BN) : nkt_all;
-  const int kt0 = (int)((int64_t)s * nkt / ns);
-  const int kt1 = (int)((int64_t)(s + 1) * nkt / ns);
+  const int kt0 = RUNS ? seg_kb : (int)((int64_t)s * nkt / ns);
+  const int kt1 = RUNS ? seg_ke : (int)((int64_t)(s + 1) * nkt / ns);
+  const bool cut = RUNS && (seg_kb > 0 || seg_ke < seg_units);  // a segment of a tile cut between runs
 
   // direct copies: 1 KiB block b of a tile is filled by wavefront b % NW
   uint32_t gk[C::BPW], gv[C::BPW];
@@ -258,7 +290,26 @@ fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K
   const float l_tot = xhalf_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
-  if (ns > 1) {
+  if (cut) {
+    // normalised fp32 partial O (this wavefront's slice) and the row's
+    // log2-sum-exp, in the run's slot (split_slot) for the merge kernel
+    if (qi < Sq) {
+      const size_t slot = split_slot(run, tile_lin, ksp.runs, ksp.total, ksp.bias);
+      float* dst = ksp.ws_o + (slot * 32 + r32) * D + 128 * w;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int d0 = 32 * db + 8 * jg + 4 * hh;
+          *reinterpret_cast<f32x4*>(dst + d0) = f32x4{oacc[db][4 * jg] * inv, oacc[db][4 * jg + 1] * inv,
+                                                      oacc[db][4 * jg + 2] * inv, oacc[db][4 * jg + 3] * inv};
+        }
+      if (w == 0 && hh == 0) ksp.ws_lse[slot * 32 + r32] = l_tot > 0.f ? m_run + __builtin_log2f(l_tot) : kNegInf;
+    }
+    __syncthreads();  // every wavefront is done with LDS before the next segment's copies
+    continue;
+  }
+  if (!RUNS && ns > 1) {
     // partial for key part s: normalised O_s (fp32) and lse_s, rows of
     // [BH * Sq, ns, D]
     if (qi < Sq) {
@@ -303,6 +354,9 @@ fwd_splitd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K
                 *reinterpret_cast<const u32x4*>(tile + swz<16>(row, c)));
   }
   if (w == 0 && hh == 0 && qi < Sq) LSE[(size_t)bh * Sq + qi] = lse;
+  if constexpr (!RUNS) return;
+  __syncthreads();  // the next segment refills LDS
+  }
 }
 
 }  // namespace fa

@@ -160,8 +160,9 @@ def test_auto_splits(lib, B, H, Sk, cus, want):
     (1, 4, 2048, 2048, 256, 0, 256, 4),    # 64 tiles on 256 CUs: four runs each
     (1, 2, 1000, 1000, 256, 1, 256, 8),    # 16 tiles on 256 CUs: runs of 5 key tiles
     (8, 32, 2048, 2048, 256, 1, 256, 1),   # 4096 tiles: more than two per CU, never split
-    (1, 4, 512, 512, 1024, 0, 256, 4),     # Split-D: 64 work items -> 4 parts
+    (1, 4, 512, 512, 1024, 0, 256, 4),     # Split-D: 64 work items -> runs of a quarter tile
     (1, 8, 1024, 1024, 512, 0, 256, 1),    # Split-D: 256 work items fill the CUs
+    (1, 8, 1024, 1024, 512, 1, 256, 2),    # Split-D causal: runs, every heavy tile cut once
     (0, 1, 16, 16, 256, 0, 256, 0),        # invalid sizes
     (1, 1, 16, 16, 96, 0, 256, 0),
     (1, 1, 16, 16, 256, 2, 256, 0),
@@ -270,11 +271,14 @@ def test_fwd_workspace_bytes(lib, B, H, Sq, Sk, D, causal, cus):
         assert ws == 0
     elif Sq == 1 and not causal:
         assert ws == lib.fa_decode_workspace_bytes(B, H, D, ns) == rup256(B * H * ns * (D + 1) * 4)
-    elif D >= 512:
-        assert ws == rup256(B * H * Sq * ns * (D + 1) * 4)
-    elif D == 256:
-        # runs: partial O and log2-sum-exp slots for two segments of each of G runs
-        assert any(ws == rup256(g * 2 * 128 * D * 4) + rup256(g * 2 * 128 * 4) for g in range(1, 2 * cus + 9)), ws
+    elif D >= 256:
+        # runs (32-row tiles for Split-D, 128-row at D = 256): partial O and
+        # log2-sum-exp slots for two segments of each of G runs; or, for
+        # Split-D, equal key parts of every query row
+        bm = 32 if D >= 512 else 128
+        runs = any(ws == rup256(g * 2 * bm * D * 4) + rup256(g * 2 * bm * 4) for g in range(1, 2 * cus + 9))
+        parts = D >= 512 and ws == rup256(B * H * Sq * ns * (D + 1) * 4)
+        assert runs or parts, ws
     else:
         # rows of the split 128-row query tiles: a whole number of tiles per slice
         assert ws % 256 == 0 and ws > 0
