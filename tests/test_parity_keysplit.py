@@ -11,8 +11,9 @@ this device, so these tests run the split kernels and their merges; the bar
 is the one of every prefill: max |dO| <= 2e-3, max |dLSE| <= 1e-3.  Also
 covered: bitwise repeatability, split calls of different workspace sizes
 queued without a sync, split calls on two streams at once (each with its own
-pool workspace), and fa_fwd_ws with a caller workspace (bit-identical to
-fa_fwd; a short workspace is refused).
+pool workspace), fa_fwd_ws with a caller workspace (bit-identical to fa_fwd;
+a short workspace is refused), a caller workspace reused across calls and
+holding arbitrary bytes, and a captured graph of one split call replayed.
 """
 import math
 
@@ -225,3 +226,64 @@ def test_fwd_ws_caller_workspace_matches_fwd(env):
     torch.cuda.synchronize()
     O, L = oracle.attention(q, k, v, False, 0.125)
     check(o, lse, O, L, "fa_fwd_ws without workspace")
+
+
+def test_fwd_ws_workspace_reuse_and_contents(env):
+    # one caller workspace for a sequence of D = 256 split calls: first
+    # filled with 0xff bytes, then reused without clearing for other inputs,
+    # then filled with random bytes; nothing a call reads from it is left
+    # from an earlier call, so every call matches the oracle and equal inputs
+    # give bit-identical outputs
+    torch, dev, fa, cus = env
+    shape = (1, 8, 1024, 1024)
+    nbytes = fa.fa_fwd_workspace_bytes(*shape, D, True, cus)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=dev)
+    cases = [inputs(env, *shape, True, seed=s) for s in (81, 82)]
+    refs = [oracle.attention(*host, True, 1 / 16) for host, _, _ in cases]
+    first = fa.fa_fwd_ws(*cases[0][1], ws, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    check(*first, *refs[0], "workspace of 0xff bytes")
+    for rep in range(3):  # queued without a sync, one workspace
+        outs = [fa.fa_fwd_ws(*dev_in, ws, causal=True, scale=1 / 16) for _, dev_in, _ in cases]
+        torch.cuda.synchronize()
+        for i, out in enumerate(outs):
+            check(*out, *refs[i], f"reused workspace, call {rep}.{i}")
+        assert torch.equal(outs[0][0], first[0]) and torch.equal(outs[0][1], first[1])
+    ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev))
+    again = fa.fa_fwd_ws(*cases[0][1], ws, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1])
+
+
+def test_fwd_ws_split_call_graph_replays(env):
+    # one D = 256 split call (split kernel and merge kernel) captured in a
+    # graph and replayed; each replay (with eager work and a sync in
+    # between) is bit-identical to the eager call
+    torch, dev, fa, cus = env
+    shape = (1, 8, 1024, 1024)
+    host, dev_in, ns = inputs(env, *shape, True, seed=91)
+    nbytes = fa.fa_fwd_workspace_bytes(*shape, D, True, cus)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(dev_in[0])
+    lse = torch.empty(dev_in[0].shape[:3], dtype=torch.float32, device=dev)
+    eager = fa.fa_fwd_ws(*dev_in, ws, causal=True, scale=1 / 16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_fwd_ws(*dev_in, ws, o, lse, causal=True, scale=1 / 16)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_fwd_ws(*dev_in, ws, o, lse, causal=True, scale=1 / 16)
+    for rep in range(4):
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager[0]) and torch.equal(lse, eager[1]), f"replay {rep}"
+        fa.fa_fwd_ws(*dev_in, ws, causal=True, scale=1 / 16)  # eager work between replays
+        torch.cuda.synchronize()
+    O, L = oracle.attention(*host, True, 1 / 16)
+    check(o, lse, O, L, f"graph replay ns={ns}")
