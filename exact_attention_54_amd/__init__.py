@@ -25,6 +25,8 @@ __all__ = [
     "fa_fwd_workspace_bytes",
     "fa_fwd_varlen",
     "fa_bwd",
+    "fa_bwd_ws",
+    "fa_bwd_workspace_bytes",
     "fa_decode_splitkv",
     "fa_decode_splitkv_ws",
     "fa_decode_paged",
@@ -127,6 +129,21 @@ def fa_fwd_workspace_bytes(B, H, Sq, Sk, D, causal, num_cus):
 
 def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, causal=False, scale=None, stream=None):
     """Gradients (dq, dk, dv) of exact attention from fa_fwd's o and lse.  See fa_bwd in include/fa.h."""
+    return _bwd(q, k, v, o, lse, do, dq, dk, dv, causal, scale, stream, None, False)
+
+
+def fa_bwd_ws(q, k, v, o, lse, do, workspace, dq=None, dk=None, dv=None, causal=False, scale=None, stream=None):
+    """fa_bwd with a caller-owned workspace tensor (contiguous, on q's device) of at least
+    fa_bwd_workspace_bytes(B, H, Sq, D) bytes.  Nothing is allocated.  See fa_bwd_ws in include/fa.h."""
+    return _bwd(q, k, v, o, lse, do, dq, dk, dv, causal, scale, stream, workspace, True)
+
+
+def fa_bwd_workspace_bytes(B, H, Sq, D):
+    """Workspace bytes of fa_bwd / fa_bwd_ws for these sizes (0: invalid sizes)."""
+    return int(_capi.load().fa_bwd_workspace_bytes(B, H, Sq, D))
+
+
+def _bwd(q, k, v, o, lse, do, dq, dk, dv, causal, scale, stream, workspace, with_ws):
     torch = _torch()
     B, H, Sq, Sk, D = _check_qkv(q, k, v)
     for name, t, shape in (("o", o, q.shape), ("do", do, q.shape)):
@@ -144,10 +161,16 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, causal=False, scale=N
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     lib = _capi.load()
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
-                    _stream(q, stream))
-    _capi.check(st, "fa_bwd")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
+            _stream(q, stream))
+    if with_ws:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        st = lib.fa_bwd_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        _capi.check(st, "fa_bwd_ws")
+    else:
+        _capi.check(lib.fa_bwd(*args), "fa_bwd")
     return dq, dk, dv
 
 

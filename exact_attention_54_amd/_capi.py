@@ -27,6 +27,8 @@ SIGNATURES = {
     "fa_fwd_ws": (_I, _COMMON + [_P, _S]),
     "fa_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_bwd_ws": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _I, _F, _P, _P, _S]),
+    "fa_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_decode_splitkv": (_I, _COMMON + [_I]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),

@@ -947,6 +947,43 @@ int pool_alloc(size_t bytes, hipStream_t s, void** out) {
   return hip_check(hipMallocFromPoolAsync(out, bytes, pool, s), "workspace allocation");
 }
 
+// Row workspace of the backward: D and the LSE in log2 units, one fp32 each
+// per query row.
+size_t bwd_row_bytes(int64_t BH, int Sq) { return ((size_t)BH * Sq * 8 + 255) / 256 * 256; }
+
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D, int causal, float scale) {
+  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
+  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 32, 64, 128 and 256");
+  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  return FA_OK;
+}
+
+// The backward's kernels on the per-row workspace `ws`.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+            void* dk, void* dv, int B, int H, int Sq, int Sk, int D, int causal, float scale, hipStream_t s, void* ws) {
+  const int BH = B * H;
+  float* dvec = static_cast<float*>(ws);
+  switch (D) {
+    case 32:
+      return causal ? launch_bwd<32, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                    : launch_bwd<32, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+    case 64:
+      return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                    : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+    case 128:
+      return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                    : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+    default:
+      return causal ? launch_bwd<256, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
+                    : launch_bwd<256, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -1023,43 +1060,37 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D, int causal, float scale,
            void* stream) {
-  int rc = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale);
+  int rc = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Sq, Sk, D, causal, scale);
   if (rc != FA_OK) return rc;
-  if (!dout || !dq || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "null gradient pointer");
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-    return fail(FA_ERR_INVALID_ARG, "dout, dq, dk, dv must be 16-byte aligned");
-  if (D > 256) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dims 32, 64, 128 and 256");
-  if ((int64_t)B * H > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;
   rc = workspace_pool(&pool);
   if (rc != FA_OK) return rc;
   void* ws = nullptr;
-  const size_t bytes = ((size_t)B * H * Sq * 8 + 255) / 256 * 256;  // D and LSE in log2 units
-  rc = hip_check(hipMallocFromPoolAsync(&ws, bytes, pool, s), "workspace allocation");
+  rc = hip_check(hipMallocFromPoolAsync(&ws, bwd_row_bytes((int64_t)B * H, Sq), pool, s), "workspace allocation");
   if (rc != FA_OK) return rc;
-  float* dvec = static_cast<float*>(ws);
-  const int BH = B * H;
-  switch (D) {
-    case 32:
-      rc = causal ? launch_bwd<32, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                  : launch_bwd<32, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
-      break;
-    case 64:
-      rc = causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                  : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
-      break;
-    case 128:
-      rc = causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                  : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
-      break;
-    default:
-      rc = causal ? launch_bwd<256, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec)
-                  : launch_bwd<256, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, Sq, Sk, scale, s, dvec);
-      break;
-  }
+  rc = run_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Sq, Sk, D, causal, scale, s, ws);
   const int frc = hip_check(hipFreeAsync(ws, s), "hipFreeAsync workspace");
   return rc != FA_OK ? rc : frc;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D) {
+  if (B < 1 || H < 1 || Sq < 1) return 0;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return 0;
+  return bwd_row_bytes((int64_t)B * H, Sq);
+}
+
+int fa_bwd_ws(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D, int causal, float scale,
+              void* stream, void* workspace, size_t workspace_bytes) {
+  int rc = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Sq, Sk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  if (!workspace || !aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace must be non-null and 16-byte aligned");
+  const size_t need = bwd_row_bytes((int64_t)B * H, Sq);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Sq, Sk, D, causal, scale, static_cast<hipStream_t>(stream),
+                 workspace);
 }
 
 int fa_fwd_key_splits(int B, int H, int Sq, int Sk, int D, int causal, int num_cus) {

@@ -147,14 +147,35 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
  * with P = exp(scale * Q K^T + mask - lse), dP = dout V^T.  All tensors are
  * caller-owned device memory, 16-byte aligned (lse 4-byte); outputs must not
  * overlap inputs.  A per-row workspace (D and the LSE in log2 units,
- * 2*B*H*Sq fp32) comes from the same
- * per-device pool as fa_decode_splitkv.  Three kernels run on `stream`.
- * Supports D in {32, 64, 128, 256} (other D: FA_ERR_UNSUPPORTED); other
- * errors as fa_fwd.
+ * fa_bwd_workspace_bytes) comes from the same per-device pool as
+ * fa_decode_splitkv.  Three kernels run on `stream`: D_i, then dK and dV,
+ * then dQ (the dK/dV and the dQ kernel each form S, P, dP and dS of their
+ * tiles, so no partial sums cross workgroups and the result is bitwise
+ * repeatable).  Supports D in {32, 64, 128, 256} (other D:
+ * FA_ERR_UNSUPPORTED); other errors as fa_fwd.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
            int causal, float scale, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace of fa_bwd / fa_bwd_ws: one fp32
+ * D and one fp32 LSE (log2 units) per query row, 2 * B * H * Sq * 4 bytes
+ * rounded up to 256.  Pure host arithmetic; 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int D);
+
+/*
+ * fa_bwd_ws -- fa_bwd with a caller-provided device workspace of at least
+ * fa_bwd_workspace_bytes(B, H, Sq, D) bytes, 16-byte aligned (a null,
+ * misaligned or smaller one returns FA_ERR_INVALID_ARG before any launch).
+ * Nothing is allocated; same kernels and results as fa_bwd.  Calls that
+ * share one workspace must be ordered on one stream; the workspace holds no
+ * result.
+ */
+int fa_bwd_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, int B, int H, int Sq, int Sk, int D,
+              int causal, float scale, void* stream, void* workspace, size_t workspace_bytes);
 
 /*
  * fa_fwd_varlen -- fa_fwd over a packed batch of variable-length sequences

@@ -421,6 +421,35 @@ def test_bwd_rejects_head_dims_without_a_kernel(lib, D):
     assert "head dim" in _capi.last_error()
 
 
+@pytest.mark.parametrize("B,H,Sq,D", [(1, 32, 4096, 128), (2, 3, 5, 64), (1, 2, 129, 32), (1, 16, 2048, 256)])
+def test_bwd_workspace_bytes(lib, B, H, Sq, D):
+    # one fp32 D and one fp32 LSE (log2 units) per query row
+    assert lib.fa_bwd_workspace_bytes(B, H, Sq, D) == rup256(B * H * Sq * 8)
+
+
+def test_bwd_workspace_bytes_invalid(lib):
+    assert lib.fa_bwd_workspace_bytes(0, 1, 16, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 16, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 16, 512) == 0
+
+
+def test_bwd_ws_rejects_before_any_hip_call(lib):
+    a = GOOD
+    need = lib.fa_bwd_workspace_bytes(a["B"], a["H"], a["Sq"], a["D"])
+
+    def call(ws, nbytes, **kw):
+        b = dict(a, **kw)
+        return lib.fa_bwd_ws(P[0], P[1], P[2], P[3], P[4], A + 0x5000, A + 0x6000, A + 0x7000, A + 0x8000, b["B"],
+                             b["H"], b["Sq"], b["Sk"], b["D"], b["causal"], b["scale"], None, ws, nbytes)
+
+    assert call(None, need) == _capi.FA_ERR_INVALID_ARG          # no workspace
+    assert call(A + 0x9008, need) == _capi.FA_ERR_INVALID_ARG    # misaligned workspace
+    assert call(A + 0x9000, need - 1) == _capi.FA_ERR_INVALID_ARG  # one byte short
+    assert "workspace" in _capi.last_error()
+    assert call(A + 0x9000, need, D=512) == _capi.FA_ERR_UNSUPPORTED
+    assert call(A + 0x9000, need, scale=0.0) == _capi.FA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("D", [512, 1024])
 def test_large_heads_only_through_fa_fwd(lib, D):
     # Split-D serves fa_fwd; decoding, paged decoding, packed prefill and the

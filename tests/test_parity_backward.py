@@ -1,4 +1,4 @@
-"""GPU parity of the backward pass (fa_bwd) against the CPU fp64 oracle.
+"""GPU parity of the backward pass (fa_bwd, fa_bwd_ws) against the CPU fp64 oracle.
 
 The GPU pass takes o and lse from the GPU forward and the fp16 dO; the
 oracle differentiates the definition in fp64 from the same fp16 q, k, v, dO.
@@ -159,3 +159,29 @@ def test_backward_errors_raise(torch_dev, fa):
     with pytest.raises(fa.FAError) as e:
         fa.fa_bwd(q, q, q, o, lse, q)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+def test_backward_ws_matches_fa_bwd(torch_dev, fa):
+    # fa_bwd_ws with a caller workspace (first filled with 0xff bytes, then
+    # reused for a second shape) gives fa_bwd's results bit for bit; a
+    # workspace one byte short is refused before any launch
+    torch, dev = torch_dev
+    D = 64
+    shapes = [(1, 2, 300, 300), (2, 1, 129, 65)]
+    nbytes = max(fa.fa_bwd_workspace_bytes(B, H, Sq, D) for B, H, Sq, _ in shapes)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=dev)
+    for i, (B, H, Sq, Sk) in enumerate(shapes):
+        q, k, v = make_qkv(B, H, Sq, Sk, D, 90 + i)
+        do = make_qkv(B, H, Sq, 1, D, 95 + i)[0]
+        qd, kd, vd, dod = (torch.from_numpy(x).to(dev) for x in (q, k, v, do))
+        o, lse = fa.fa_fwd(qd, kd, vd, causal=True, scale=0.125)
+        a = fa.fa_bwd(qd, kd, vd, o, lse, dod, causal=True, scale=0.125)
+        b = fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws, causal=True, scale=0.125)
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(a, b)), (B, H, Sq, Sk)
+        check([x.float().cpu().numpy() for x in b], oracle.attention_backward(q, k, v, do, True, 0.125),
+              term_magnitudes(q, k, v, do, True, 0.125), f"bwd_ws {(B, H, Sq, Sk)}")
+    short = fa.fa_bwd_workspace_bytes(shapes[-1][0], shapes[-1][1], shapes[-1][2], D) - 1
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws[:short], causal=True, scale=0.125)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
