@@ -177,6 +177,7 @@ def roofline_context(torch, dev, buf, cus, warmup):
     lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_54_amd", "libroofline_probe.so"))
     lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_empty_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     st = torch.cuda.current_stream(dev).cuda_stream
     nbytes = buf.numel() * buf.element_size()
     rblocks, mblocks, iters = 16 * cus, 2 * cus, 4096
@@ -188,14 +189,34 @@ def roofline_context(torch, dev, buf, cus, warmup):
     def mfma():
         assert lib.probe_mfma_loop(mblocks, iters, sink.data_ptr(), st) == 0
 
+    def empty():  # the grid of the small (8, 16, 256, 256, 64) prefill: 256 blocks of 256 threads
+        assert lib.probe_empty_launch(256, 256, sink.data_ptr(), st) == 0
+
     for _ in range(max(warmup, 3)):
         read()
         mfma()
+        empty()
     t_read = time_launches(torch, read, 10)
     t_mfma = time_launches(torch, mfma, 10)
+    # back-to-back empty launches from Python are host-bound, so 50 of them
+    # are captured in a graph and the replay is timed: launch cost on the GPU
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        empty()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gst = torch.cuda.current_stream(dev).cuda_stream
+        for _ in range(50):
+            assert lib.probe_empty_launch(256, 256, sink.data_ptr(), gst) == 0
+    graph.replay()
+    t_empty = time_launches(torch, graph.replay, 5) / 50
     mfma_flops = mblocks * 4 * iters * 8 * 32768.0   # 4 wavefronts per block, 8 MFMAs per round
     return {"context_stream_read_gbps": round(nbytes / t_read / 1e9, 1),
-            "context_mfma_loop_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
+            "context_mfma_loop_tflops": round(mfma_flops / t_mfma / 1e12, 1),
+            "context_empty_launch_us": round(t_empty * 1e6, 2)}
 
 
 def blas_threads():
@@ -585,7 +606,8 @@ def main():
     # on this GPU right now (exact_attention_54_amd/csrc/roofline_probe.hip).
     context = roofline_context(torch, dev, k4, cus, args.warmup)
     log(f"context: plain HBM read stream {context['context_stream_read_gbps']:.1f} GB/s; "
-        f"plain fp16 MFMA loop {context['context_mfma_loop_tflops']:.1f} TFLOPS")
+        f"plain fp16 MFMA loop {context['context_mfma_loop_tflops']:.1f} TFLOPS; "
+        f"empty 256 x 256 launch {context['context_empty_launch_us']:.2f} us")
 
     src_hash = kernel_source_hash()
     roof_pre = {

@@ -10,8 +10,12 @@
 //   probe_mfma_loop    every wavefront runs `iters` rounds of 8 independent
 //                      v_mfma_f32_32x32x16_f16 (32768 FLOP each) on register
 //                      operands and writes one value per lane to `sink`.
+//   probe_empty_launch a grid that does no work (thread 0 of each block
+//                      writes one float to `sink`): what a launch of that
+//                      shape costs by itself, the floor under the smallest
+//                      attention grids.
 //
-// Both are asynchronous on `stream` and return 0, or 1 if the launch failed.
+// All are asynchronous on `stream` and return 0, or 1 if the launch failed.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -75,6 +79,10 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) mfma_loop_kernel(float* __res
   sink[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = s;
 }
 
+__global__ void empty_kernel(float* __restrict__ sink) {
+  if (threadIdx.x == 0) sink[blockIdx.x] = 0.f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +101,13 @@ int probe_mfma_loop(int blocks, int iters, float* sink, void* stream) {
   if (!sink || blocks < 1 || iters < 1) return 1;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(kMfmaThreads), 0, static_cast<hipStream_t>(stream), sink,
                      iters);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// sink: device floats, one per block; threads a multiple of 64, at most 1024.
+int probe_empty_launch(int blocks, int threads, float* sink, void* stream) {
+  if (!sink || blocks < 1 || threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
+  hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(threads), 0, static_cast<hipStream_t>(stream), sink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
