@@ -376,24 +376,22 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    # events around every launch inside the timed loop: the per-kernel
-    # averages are taken under the same conditions as the step time
-    ev = [[TimingEvent(torch) for _ in range(3)] for _ in range(args.steps)]
-    start = TimingEvent(torch)
-    end = TimingEvent(torch)
+    # one event between consecutive launches inside the timed loop: launch
+    # j runs between events j and j + 1, so the per-kernel averages are taken
+    # under the same conditions as the step time, and the first and last
+    # events bracket the whole timed region
+    ev = [TimingEvent(torch) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    ev[0].record()
     for i in range(args.steps):
-        ev[i][0].record()
         prefill()
-        ev[i][1].record()
+        ev[2 * i + 1].record()
         decode()
-        ev[i][2].record()
-    end.record()
+        ev[2 * i + 2].record()
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    t_pre = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps * 1e-3
+    t_dec = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps * 1e-3
     flops = prefill_flops(w3.B, w3.H, w3.Sq, w3.Sk, w3.D, True)
     kv_bytes = 2.0 * w4.B * w4.H * w4.Sk * w4.D * 2
     tflops = flops / t_pre / 1e12
