@@ -279,7 +279,8 @@ SplitPlan plan_fwd_runs(int nqt, int BH, int BM, int BN, int D, int Sq, int Sk, 
   // seventh of the longest tile
   int64_t runs = std::min<int64_t>(cus, total / 4);
   runs = std::min<int64_t>(runs, 7 * total / umax);
-  if (runs < 2) return best;
+  // the run boundaries are computed in 32-bit unsigned arithmetic
+  if (runs < 2 || (runs + 8) * total >= ((int64_t)1 << 32)) return best;
   const int len = (int)(total / runs);  // shortest run before the bias
   const int step = std::max(1, (len / 4) / 8);
   for (int bias = 0; bias <= len / 4; bias += step) {

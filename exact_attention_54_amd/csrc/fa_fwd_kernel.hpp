@@ -142,12 +142,15 @@ constexpr bool split_by_runs() { return D == 256; }
 // runs start `bias` later), and the run that holds position x.  Runs are
 // floor(total / runs) or one more key tiles long before the bias, so two
 // consecutive runs cover exactly one (heavy, light) pair whenever the pairs
-// hold 2 * total / runs key tiles.
+// hold 2 * total / runs key tiles.  The planner takes runs only when
+// (runs + 8) * total < 2^32 (g <= runs + 7 for the workgroups of a grid
+// rounded up to a multiple of 8), so these products fit 32-bit unsigned
+// arithmetic (a 64-bit division costs ~140 instructions on the GPU).
 __host__ __device__ inline long long split_start(int g, int runs, int total, int bias) {
-  return (long long)g * total / runs + ((g & 1) ? bias : 0);
+  return (long long)((uint32_t)g * (uint32_t)total / (uint32_t)runs) + ((g & 1) ? bias : 0);
 }
 __host__ __device__ inline int split_run(int x, int runs, int total, int bias) {
-  int g = (int)(((long long)(x + 1) * runs - 1) / total);
+  int g = (int)(((uint32_t)(x + 1) * (uint32_t)runs - 1u) / (uint32_t)total);
   if ((g & 1) && split_start(g, runs, total, bias) > x) --g;
   return g;
 }
@@ -677,12 +680,22 @@ fwd_split_merge_kernel(KeySplit ksp, _Float16* __restrict__ O, float* __restrict
   const int rank = tile - bh * nqt;
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int u = fwd_tile_units(qt, BM, BN, Sq, Sk, CAUSAL);
-  int tile_lin = bh * ksp.units;
+  // key tiles of the slice's tiles ahead of this one in the run order, one
+  // tile per lane and summed across the wavefront
   const int pos = split_position(rank, nqt);
-  for (int i = 0; i < pos; ++i) {
-    const int r = split_order(i, nqt);
-    tile_lin += fwd_tile_units(CAUSAL ? nqt - 1 - r : r, BM, BN, Sq, Sk, CAUSAL);
+  const int lane = (int)threadIdx.x & 63;
+  int before = 0;
+  for (int i0 = 0; i0 < pos; i0 += 64) {
+    int ui = 0;
+    if (i0 + lane < pos) {
+      const int r = split_order(i0 + lane, nqt);
+      ui = fwd_tile_units(CAUSAL ? nqt - 1 - r : r, BM, BN, Sq, Sk, CAUSAL);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ui += __shfl_xor(ui, off);
+    before += ui;
   }
+  const int tile_lin = bh * ksp.units + before;
   const int g0 = split_run(tile_lin, ksp.runs, ksp.total, ksp.bias);
   const int g1 = split_run(tile_lin + u - 1, ksp.runs, ksp.total, ksp.bias);
   if (g0 == g1) return;  // written whole by its run
