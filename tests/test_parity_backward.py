@@ -1,4 +1,5 @@
-"""GPU parity of the backward pass (fa_bwd, fa_bwd_ws) against the CPU fp64 oracle.
+"""GPU parity of the backward pass (fa_bwd, fa_bwd_ws) against the CPU fp64 oracle;
+fa_bwd_ws is also checked bit for bit against fa_bwd and under graph replay.
 
 The GPU pass takes o and lse from the GPU forward and the fp16 dO; the
 oracle differentiates the definition in fp64 from the same fp16 q, k, v, dO.
@@ -185,3 +186,37 @@ def test_backward_ws_matches_fa_bwd(torch_dev, fa):
     with pytest.raises(fa.FAError) as e:
         fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws[:short], causal=True, scale=0.125)
     assert e.value.status == fa.FA_ERR_INVALID_ARG
+
+
+def test_backward_ws_graph_replays(torch_dev, fa):
+    # fa_bwd_ws (three kernels, no allocation) captured in a graph and
+    # replayed; each replay, with eager work and a sync in between, is
+    # bit-identical to the eager call
+    torch, dev = torch_dev
+    B, H, S, D = 1, 4, 384, 128
+    q, k, v = make_qkv(B, H, S, S, D, 97)
+    do = make_qkv(B, H, S, 1, D, 98)[0]
+    qd, kd, vd, dod = (torch.from_numpy(x).to(dev) for x in (q, k, v, do))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=True, scale=0.1)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, D), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    eager = fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws, causal=True, scale=0.1)
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in eager]
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws, *grads, causal=True, scale=0.1)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws, *grads, causal=True, scale=0.1)
+    for rep in range(3):
+        for x in grads:
+            x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(grads, eager)), f"replay {rep}"
+        fa.fa_bwd_ws(qd, kd, vd, o, lse, dod, ws, causal=True, scale=0.1)  # eager work between replays
+        torch.cuda.synchronize()
