@@ -44,13 +44,44 @@ __all__ = [
 ]
 
 
-def _torch():
-    import torch
+_TORCH = None
+_F16 = None
+_F32 = None
+_RAW_STREAM = None
 
-    return torch
+
+def _torch():
+    global _TORCH, _F16, _F32, _RAW_STREAM
+    if _TORCH is None:
+        import torch
+
+        _F16, _F32 = torch.float16, torch.float32
+        # the current stream's handle as an int, without building a Stream object
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _TORCH = torch
+    return _TORCH
 
 
 def _check_qkv(q, k, v):
+    """(B, H, Sq, Sk, D) of fp16, contiguous, 4-d q, k, v on one GPU.  The
+    common valid case is settled by one chain of cheap attribute tests; any
+    failure re-runs the checks one by one for a precise message."""
+    _torch()
+    try:
+        qs, ks = q.shape, k.shape
+        dev = q.get_device()
+        if (len(qs) == 4 and len(ks) == 4 and dev >= 0
+                and q.dtype is _F16 and k.dtype is _F16 and v.dtype is _F16
+                and k.get_device() == dev and v.get_device() == dev
+                and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+                and v.shape == ks and ks[0] == qs[0] and ks[1] == qs[1] and ks[3] == qs[3]):
+            return qs[0], qs[1], qs[2], ks[2], qs[3]
+    except (AttributeError, TypeError):
+        pass
+    return _check_qkv_slow(q, k, v)
+
+
+def _check_qkv_slow(q, k, v):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
@@ -71,14 +102,32 @@ def _check_qkv(q, k, v):
 
 def _outputs(q, o, lse):
     torch = _torch()
-    B, H, Sq, D = q.shape
+    qs = q.shape
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if o.dtype != torch.float16 or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous() or o.device != q.device:
+        lse = torch.empty((qs[0], qs[1], qs[2]), dtype=_F32, device=q.device)
+    try:
+        dev = q.get_device()
+        ls = lse.shape
+        if (o.dtype is _F16 and lse.dtype is _F32 and o.shape == qs and len(ls) == 3
+                and ls[0] == qs[0] and ls[1] == qs[1] and ls[2] == qs[2]
+                and o.get_device() == dev and lse.get_device() == dev
+                and o.is_contiguous() and lse.is_contiguous()):
+            return o, lse
+    except (AttributeError, TypeError):
+        pass
+    return _outputs_slow(q, o, lse)
+
+
+def _outputs_slow(q, o, lse):
+    torch = _torch()
+    B, H, Sq, D = q.shape
+    if not isinstance(o, torch.Tensor) or o.dtype != torch.float16 or tuple(o.shape) != tuple(q.shape) \
+            or not o.is_contiguous() or o.device != q.device:
         raise ValueError("o must be a contiguous fp16 tensor shaped like q on its device")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous() or lse.device != q.device:
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) \
+            or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 [B, H, Sq] tensor on q's device")
     return o, lse
 
@@ -86,6 +135,8 @@ def _outputs(q, o, lse):
 def _stream(q, stream):
     torch = _torch()
     if stream is None:
+        if _RAW_STREAM is not None:
+            return _RAW_STREAM(q.get_device())
         stream = torch.cuda.current_stream(q.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -112,7 +163,7 @@ def fa_fwd_ws(q, k, v, workspace, o=None, lse=None, causal=False, scale=None, st
         scale = 1.0 / math.sqrt(D)
     ptr, nbytes = 0, 0
     if workspace is not None:
-        if not workspace.is_contiguous() or workspace.device != q.device:
+        if not workspace.is_contiguous() or workspace.get_device() != q.get_device():
             raise ValueError("workspace must be contiguous and on q's device")
         ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     lib = _capi.load()
