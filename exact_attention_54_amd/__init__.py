@@ -47,17 +47,14 @@ __all__ = [
 _TORCH = None
 _F16 = None
 _F32 = None
-_RAW_STREAM = None
 
 
 def _torch():
-    global _TORCH, _F16, _F32, _RAW_STREAM
+    global _TORCH, _F16, _F32
     if _TORCH is None:
         import torch
 
         _F16, _F32 = torch.float16, torch.float32
-        # the current stream's handle as an int, without building a Stream object
-        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
         _TORCH = torch
     return _TORCH
 
@@ -135,9 +132,7 @@ def _outputs_slow(q, o, lse):
 def _stream(q, stream):
     torch = _torch()
     if stream is None:
-        if _RAW_STREAM is not None:
-            return _RAW_STREAM(q.get_device())
-        stream = torch.cuda.current_stream(q.device)
+        stream = torch.cuda.current_stream(q.get_device())
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
