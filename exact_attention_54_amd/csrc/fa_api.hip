@@ -498,23 +498,39 @@ int launch_decode(const void* q, const void* k, const void* v, void* o, float* l
   return launched("decode merge launch");
 }
 
+template <int D, int T, bool FINAL, bool GROUP>
+void launch_paged_partial(const void* q, const void* kc, const void* vc, const int* tables, const int* seq_lens,
+                          float* ws_o, float* ws_lse, void* o, float* lse, int BH, int H, int ns, int num_blocks,
+                          int lbs, int max_blocks, float c2, hipStream_t stream) {
+  hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D, T, FINAL, GROUP>), dim3(BH * ns), dim3(T), 0, stream,
+                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(kc),
+                     static_cast<const _Float16*>(vc), tables, seq_lens, ws_o, ws_lse, static_cast<_Float16*>(o),
+                     lse, H, ns, num_blocks, lbs, max_blocks, c2);
+}
+
 template <int D>
 int launch_decode_paged(const void* q, const void* kc, const void* vc, const int* tables, const int* seq_lens,
                         void* o, float* lse, int B, int H, int num_blocks, int lbs, int max_blocks, float scale,
                         hipStream_t stream, int ns, float* ws_o, float* ws_lse) {
   const float c2 = scale * fa::kLog2e;
   const int BH = B * H;
+  // a wavefront's group of keys lies in one page: translated once per group
+  const bool group = (1 << lbs) >= fa::DecCfg<D>::KEYS_PER_WAVE_ITER;
   if (ns == 1) {
-    hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D, kDecFusedThreads, true>), dim3(BH),
-                       dim3(kDecFusedThreads), 0, stream, static_cast<const _Float16*>(q),
-                       static_cast<const _Float16*>(kc), static_cast<const _Float16*>(vc), tables, seq_lens, nullptr,
-                       nullptr, static_cast<_Float16*>(o), lse, H, 1, num_blocks, lbs, max_blocks, c2);
+    if (group)
+      launch_paged_partial<D, kDecFusedThreads, true, true>(q, kc, vc, tables, seq_lens, nullptr, nullptr, o, lse,
+                                                            BH, H, 1, num_blocks, lbs, max_blocks, c2, stream);
+    else
+      launch_paged_partial<D, kDecFusedThreads, true, false>(q, kc, vc, tables, seq_lens, nullptr, nullptr, o, lse,
+                                                             BH, H, 1, num_blocks, lbs, max_blocks, c2, stream);
     return launched("paged decode launch");
   }
-  hipLaunchKernelGGL((fa::decode_paged_partial_kernel<D, 256, false>), dim3(BH * ns), dim3(256), 0, stream,
-                     static_cast<const _Float16*>(q), static_cast<const _Float16*>(kc),
-                     static_cast<const _Float16*>(vc), tables, seq_lens, ws_o, ws_lse, nullptr, nullptr, H, ns,
-                     num_blocks, lbs, max_blocks, c2);
+  if (group)
+    launch_paged_partial<D, 256, false, true>(q, kc, vc, tables, seq_lens, ws_o, ws_lse, nullptr, nullptr, BH, H, ns,
+                                              num_blocks, lbs, max_blocks, c2, stream);
+  else
+    launch_paged_partial<D, 256, false, false>(q, kc, vc, tables, seq_lens, ws_o, ws_lse, nullptr, nullptr, BH, H,
+                                               ns, num_blocks, lbs, max_blocks, c2, stream);
   int rc = launched("paged decode phase-one launch");
   if (rc != FA_OK) return rc;
   launch_decode_merge<D>(BH, ns, stream, ws_o, ws_lse, static_cast<_Float16*>(o), lse);

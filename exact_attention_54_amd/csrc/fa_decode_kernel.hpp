@@ -22,6 +22,8 @@
 // writes the final fp16 O and LSE: no workspace and no second kernel.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 
 namespace fa {
@@ -39,40 +41,146 @@ struct DecCfg {
   static constexpr int NSTATE = NWAVES * SLOTS;          // independent softmax states per workgroup
 };
 
-// Online softmax of one lane slot over the keys [kb, ke) that this
-// wavefront visits (keys base + u * SLOTS + slot, base stepping by the
-// workgroup's stride).  row_of(key) is the element offset of the key's K and
-// V rows, or -1 for a key that is absent (it then scores -inf).
-template <int D, int T, class RowOf>
-__device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::CPL][8],
-                                                  const _Float16* __restrict__ kp,
-                                                  const _Float16* __restrict__ vp, int kb, int ke,
-                                                  RowOf row_of, int w, int slot, int dl, float c2,
-                                                  float& m_run, float& l_run,
-                                                  float (&acc)[DecCfg<D>::CPL][8]) {
+// Where the K and V rows of a group of keys live.  decode_accumulate walks
+// groups of KEYS_PER_WAVE_ITER consecutive keys (one per wavefront and
+// step, starting at a wave-uniform key `base`); a loader fills kr / vr with
+// the 16-byte chunks of this lane's keys base + u * SLOTS + slot whose
+// present[u] is set, clears present[u] for keys it finds absent, and leaves
+// zeros elsewhere.
+
+// Contiguous rows: key j of the slice is row j of k / v.
+template <int D, int T>
+struct ContigRows {
   using C = DecCfg<D, T>;
-  for (int base = kb + w * C::KEYS_PER_WAVE_ITER; base < ke; base += C::KEYS_PER_WG_ITER) {
-    u32x4 kr[C::U][C::CPL], vr[C::U][C::CPL];
-    bool present[C::U];
+  const _Float16* __restrict__ k;
+  const _Float16* __restrict__ v;
+  int slot, dl;
+  __device__ __forceinline__ void start(int) {}
+  __device__ __forceinline__ void operator()(int base, bool (&present)[C::U], u32x4 (&kr)[C::U][C::CPL],
+                                             u32x4 (&vr)[C::U][C::CPL]) const {
 #pragma unroll
-    for (int u = 0; u < C::U; ++u) {
-      const int key = base + u * C::SLOTS + slot;
-      const int64_t row = (key < ke) ? row_of(key) : -1;
-      present[u] = row >= 0;
+    for (int u = 0; u < C::U; ++u)
 #pragma unroll
       for (int c = 0; c < C::CPL; ++c) {
         u32x4 tk = {0u, 0u, 0u, 0u}, tv = {0u, 0u, 0u, 0u};
         if (present[u]) {
           // read once: non-temporal loads keep the stream from evicting
           // useful cache lines (measured ~13% more HBM bandwidth)
+          const size_t off = (size_t)(base + u * C::SLOTS + slot) * D + (dl + c * C::LPK) * 8;
+          tk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+          tv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+        }
+        kr[u][c] = tk;
+        vr[u][c] = tv;
+      }
+  }
+};
+
+// Paged rows, one page per lane's key: the general case (pages shorter
+// than a group).  tbl holds the physical pages of logical blocks blk0 ...;
+// an entry outside [0, num_blocks) marks its keys absent.
+template <int D, int T>
+struct PagedLaneRows {
+  using C = DecCfg<D, T>;
+  const _Float16* __restrict__ k;
+  const _Float16* __restrict__ v;
+  const int* tbl;
+  int blk0, end, num_blocks, H, h, lbs, slot, dl;
+  __device__ __forceinline__ void start(int) {}
+  __device__ __forceinline__ void operator()(int base, bool (&present)[C::U], u32x4 (&kr)[C::U][C::CPL],
+                                             u32x4 (&vr)[C::U][C::CPL]) const {
+    const int bmask = (1 << lbs) - 1;
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const int key = base + u * C::SLOTS + slot;
+      int64_t row = -1;
+      if (present[u]) {
+        const int pb = tbl[(key >> lbs) - blk0];
+        if ((unsigned)pb < (unsigned)num_blocks) row = (((int64_t)pb * H + h) << lbs) + (key & bmask);
+      }
+      present[u] = row >= 0;
+#pragma unroll
+      for (int c = 0; c < C::CPL; ++c) {
+        u32x4 tk = {0u, 0u, 0u, 0u}, tv = {0u, 0u, 0u, 0u};
+        if (present[u]) {
           const size_t off = (size_t)row * D + (dl + c * C::LPK) * 8;
-          tk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
-          tv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+          tk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+          tv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
         }
         kr[u][c] = tk;
         vr[u][c] = tv;
       }
     }
+  }
+};
+
+// Paged rows when a page holds at least one whole group (block size >=
+// KEYS_PER_WAVE_ITER, groups aligned to their size): the group's page is
+// one table entry, looked up once per wavefront, and its address is
+// wave-uniform, so the lane addresses are 32-bit offsets from it (fewer
+// registers than a 64-bit row per key: the kernel keeps the contiguous
+// kernel's occupancy).  The entry of the wavefront's next group is read
+// from LDS one step ahead, so that read does not delay the group's loads.
+template <int D, int T>
+struct PagedGroupRows {
+  using C = DecCfg<D, T>;
+  const _Float16* __restrict__ k;
+  const _Float16* __restrict__ v;
+  const int* tbl;
+  int blk0, end, num_blocks, H, h, lbs, slot, dl;
+  int next = -1;  // table entry of the group at the next call's base (lane copy)
+
+  __device__ __forceinline__ int entry(int base) const {
+    return base < end ? tbl[(base >> lbs) - blk0] : -1;
+  }
+  __device__ __forceinline__ void start(int base) { next = entry(base); }
+  __device__ __forceinline__ void operator()(int base, bool (&present)[C::U], u32x4 (&kr)[C::U][C::CPL],
+                                             u32x4 (&vr)[C::U][C::CPL]) {
+    const int pb = __builtin_amdgcn_readfirstlane(next);
+    next = entry(base + C::KEYS_PER_WG_ITER);
+    const bool ok = (unsigned)pb < (unsigned)num_blocks;
+    const size_t page = ((((size_t)pb * H + h) << lbs) + (base & ((1 << lbs) - 1))) * D;
+    const _Float16* kq = k + (ok ? page : 0);
+    const _Float16* vq = v + (ok ? page : 0);
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      present[u] = present[u] && ok;
+#pragma unroll
+      for (int c = 0; c < C::CPL; ++c) {
+        u32x4 tk = {0u, 0u, 0u, 0u}, tv = {0u, 0u, 0u, 0u};
+        if (present[u]) {
+          const int off = (u * C::SLOTS + slot) * D + (dl + c * C::LPK) * 8;
+          tk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kq + off));
+          tv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vq + off));
+        }
+        kr[u][c] = tk;
+        vr[u][c] = tv;
+      }
+    }
+  }
+};
+
+// Online softmax of one lane slot over the keys [kb, ke).  The wavefront
+// visits groups of KEYS_PER_WAVE_ITER keys starting at a0 + w * that size
+// (a0 <= kb, aligned by the caller), stepping by the workgroup's stride;
+// lane slot takes keys base + u * SLOTS + slot, and keys outside [kb, ke)
+// or absent in the loader's view score -inf.  Contiguous and paged rows
+// walk the keys in the same order, so their results agree bit for bit.
+template <int D, int T, class Load>
+__device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::CPL][8], int a0, int kb, int ke,
+                                                  Load& load, int w, int slot, float c2, float& m_run,
+                                                  float& l_run, float (&acc)[DecCfg<D>::CPL][8]) {
+  using C = DecCfg<D, T>;
+  load.start(a0 + w * C::KEYS_PER_WAVE_ITER);
+  for (int base = a0 + w * C::KEYS_PER_WAVE_ITER; base < ke; base += C::KEYS_PER_WG_ITER) {
+    u32x4 kr[C::U][C::CPL], vr[C::U][C::CPL];
+    bool present[C::U];
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const int key = base + u * C::SLOTS + slot;
+      present[u] = key >= kb && key < ke;
+    }
+    load(base, present, kr, vr);
     float sc[C::U];
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
@@ -181,7 +289,7 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
   using C = DecCfg<D, T>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int slot = lane / C::LPK;
   const int dl = lane % C::LPK;
   const int bh = blockIdx.x / ns;
@@ -219,8 +327,8 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
 
-  decode_accumulate<D, T>(qf, K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, k0, k1,
-                          [](int key) { return (int64_t)key; }, w, slot, dl, c2, m_run, l_run, acc);
+  ContigRows<D, T> rows{K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, slot, dl};
+  decode_accumulate<D, T>(qf, k0 & ~(C::KEYS_PER_WAVE_ITER - 1), k0, k1, rows, w, slot, c2, m_run, l_run, acc);
   decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
 
@@ -231,14 +339,22 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
 // logical block j (keys j*block_size .. +block_size-1) of sequence b.  The
 // workgroup of (b, h, partition) copies the table entries of its key range
 // to LDS (in segments of at most kPagedTbl blocks), then streams keys as the
-// contiguous kernel does, translating each key to its physical row.  Table
-// entries outside [0, num_blocks) mark absent keys: they are never read.
-constexpr int kPagedTbl = 1024;
+// contiguous kernel does, translating keys to physical rows.  Table entries
+// outside [0, num_blocks) mark absent keys: they are never read.
+//
+// GROUP (block_size >= KEYS_PER_WAVE_ITER): a wavefront's group of keys
+// lies in one page, translated once per group into a wave-uniform address
+// (PagedGroupRows); this form needs the registers of the contiguous kernel
+// and keeps its occupancy.  Otherwise every lane translates its own keys
+// (PagedLaneRows; held to the contiguous kernel's 64 registers, that
+// translation spills).
+constexpr int kPagedTbl = 2048;
 
-// (no occupancy target: held to 64 registers the page translation spills,
-// which measured 7% slower than one 1024-thread workgroup per CU)
-template <int D, int T, bool FINAL>
-__global__ void __launch_bounds__(T)
+template <int D, bool GROUP>
+constexpr int paged_waves_per_eu() { return GROUP ? dec_waves_per_eu<D>() : 1; }
+
+template <int D, int T, bool FINAL, bool GROUP>
+__global__ void __launch_bounds__(T, (paged_waves_per_eu<D, GROUP>()))
 decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ Kc,
                             const _Float16* __restrict__ Vc, const int* __restrict__ tables,
                             const int* __restrict__ seq_lens, float* __restrict__ ws_o,
@@ -248,7 +364,7 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
   __shared__ int s_tbl[kPagedTbl];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int slot = lane / C::LPK;
   const int dl = lane % C::LPK;
   const int bh = blockIdx.x / ns;
@@ -292,23 +408,22 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
 
   const int* trow = tables + (size_t)b * max_blocks;
-  const int bmask = (1 << lbs) - 1;
-  const int seg_keys = (kPagedTbl - 1) << lbs;  // a segment spans at most kPagedTbl blocks
-  for (int seg = k0; seg < k1; seg += seg_keys) {
+  // Segments are whole workgroup steps from the group-aligned start, so the
+  // keys meet the lanes in the contiguous kernel's order; a segment spans at
+  // most seg_keys / block_size + 1 <= kPagedTbl blocks.
+  static_assert(kPagedTbl - 1 >= C::KEYS_PER_WG_ITER, "a segment holds at least one workgroup step");
+  const int a0 = k0 & ~(C::KEYS_PER_WAVE_ITER - 1);
+  const int seg_keys = ((kPagedTbl - 1) << lbs) / C::KEYS_PER_WG_ITER * C::KEYS_PER_WG_ITER;
+  for (int seg = a0; seg < k1; seg += seg_keys) {
     const int seg_end = min(k1, seg + seg_keys);
     const int blk0 = seg >> lbs;
     const int nblk = ((seg_end - 1) >> lbs) - blk0 + 1;
     __syncthreads();  // the previous segment's table reads are done
     for (int i = tid; i < nblk; i += C::THREADS) s_tbl[i] = trow[blk0 + i];
     __syncthreads();
-    decode_accumulate<D, T>(
-        qf, Kc, Vc, seg, seg_end,
-        [&](int key) -> int64_t {
-          const int pb = s_tbl[(key >> lbs) - blk0];
-          if ((unsigned)pb >= (unsigned)num_blocks) return -1;
-          return (((int64_t)pb * H + h) << lbs) + (key & bmask);
-        },
-        w, slot, dl, c2, m_run, l_run, acc);
+    using Rows = std::conditional_t<GROUP, PagedGroupRows<D, T>, PagedLaneRows<D, T>>;
+    Rows rows{Kc, Vc, s_tbl, blk0, seg_end, num_blocks, H, h, lbs, slot, dl};
+    decode_accumulate<D, T>(qf, seg, max(seg, k0), seg_end, rows, w, slot, c2, m_run, l_run, acc);
   }
   decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }

@@ -178,6 +178,52 @@ def test_paged_8k_sampled_against_oracle(torch_dev, fa, paged_8k):
         check(o[b : b + 1, h : h + 1], lse[b : b + 1, h : h + 1], O, L, f"8k paged b={b} h={h}")
 
 
+# (D, block_size, context, ns): pages holding a whole wavefront group of keys
+# (16 keys at D = 128 and 256, 32 at D = 64, 64 at D = 32) take the
+# per-group translation, smaller pages the per-key one; ns > 1 with a context
+# that ns does not divide starts partitions between groups; 40000 / 70000
+# keys at 16-token pages and 5000 at 1-token pages stage the table in
+# several segments.
+BITWISE_CASES = [
+    (128, 16, 1000, 3),
+    (128, 4, 1000, 3),
+    (64, 32, 1000, 3),
+    (64, 16, 1000, 5),
+    (32, 64, 777, 3),
+    (32, 16, 777, 1),
+    (256, 16, 1000, 3),
+    (256, 8, 1000, 1),
+    (128, 16, 40000, 1),
+    (128, 16, 70000, 2),
+    (128, 1, 5000, 1),
+    (128, 1, 5000, 2),
+]
+
+
+@pytest.mark.parametrize("cs", BITWISE_CASES, ids=[f"D{c[0]}bs{c[1]}S{c[2]}ns{c[3]}" for c in BITWISE_CASES])
+def test_paged_matches_contiguous_bitwise(torch_dev, fa, cs):
+    # the same keys in the same order per lane: paged and contiguous decoding
+    # of one K / V agree bit for bit at any split count and page size
+    torch, _ = torch_dev
+    D, bs, S, ns = cs
+    B, H = 2, 2
+    q, k, v = make_qkv(B, H, 1, S, D, 81 + D + bs)
+    max_blocks = -(-S // bs)
+    tables, nb = paged_layout(B, max_blocks, 91 + bs, spare=3)
+    kc, vc = to_pages(k, tables, nb, bs), to_pages(v, tables, nb, bs)
+    qd, kd, vd, kcd, vcd, td = to_dev(torch_dev, q, k, v, kc, vc, tables)
+    sd = torch.full((B,), S, dtype=torch.int32, device=qd.device)
+    scale = 1.0 / np.sqrt(D)
+    op, lp = fa.fa_decode_paged(qd, kcd, vcd, td, sd, scale=scale, num_splits=ns)
+    oc, lc = fa.fa_decode_splitkv(qd, kd, vd, scale=scale, num_splits=ns)
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc), f"{cs}: O differs from contiguous decoding"
+    assert torch.equal(lp, lc), f"{cs}: LSE differs from contiguous decoding"
+    if S <= 1000:
+        O, L = oracle.decode_paged(q, kc, vc, tables, np.full(B, S, dtype=np.int32), scale)
+        check(op.float().cpu().numpy(), lp.cpu().numpy(), O, L, f"bitwise case {cs}")
+
+
 @pytest.mark.parametrize("D", [32, 128, 256])
 def test_paged_many_partitions(torch_dev, fa, D):
     # 64 partitions per slice: the merge runs its 1024-thread form (more
