@@ -541,22 +541,17 @@ template <int D, bool CAUSAL>
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, int BH, int Sq, int Sk, float scale, hipStream_t stream, float* dvec) {
   constexpr int NW = 4;
-  constexpr int LPR = (D / 8 < 16) ? D / 8 : 16;
   const int64_t rows = (int64_t)BH * Sq;
-  const int64_t dot_grid = (rows * LPR + 255) / 256;
   const int64_t kv_grid = (int64_t)((Sk + 32 * NW - 1) / (32 * NW)) * BH;
   const int nqt = (Sq + 32 * NW - 1) / (32 * NW);
   const int64_t q_grid = (int64_t)nqt * BH;
-  if (dot_grid > kMaxGrid || kv_grid > kMaxGrid || q_grid > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  if (kv_grid > kMaxGrid || q_grid > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
   const auto* Q = static_cast<const _Float16*>(q);
   const auto* K = static_cast<const _Float16*>(k);
   const auto* V = static_cast<const _Float16*>(v);
   const auto* dO = static_cast<const _Float16*>(dout);
   float* l2 = dvec + rows;  // LSE in log2 units
-  hipLaunchKernelGGL((fa::bwd_dot_kernel<D>), dim3((unsigned)dot_grid), dim3(256), 0, stream,
-                     static_cast<const _Float16*>(o), dO, lse, dvec, l2, rows);
-  int rc = launched("fa_bwd preprocess launch");
-  if (rc != FA_OK) return rc;
+  int rc = FA_OK;
   // dynamic LDS; above 64 KiB (D = 256) the kernels must be allowed it first
   constexpr int kv_dyn = fa::dkdv_lds_bytes<D, NW>();
   constexpr int q_dyn = fa::dq_lds_bytes<D, NW>();
@@ -575,13 +570,16 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
                    "fa_bwd LDS size attribute");
     if (rc != FA_OK) return rc;
   }
+  // dQ first: it also writes D and the log2 LSE of every query row, which
+  // the dK/dV kernel reads
+  hipLaunchKernelGGL(q_kern, dim3((unsigned)q_grid), dim3(64 * NW), q_dyn, stream, Q, K, V,
+                     static_cast<const _Float16*>(o), dO, lse, l2, dvec, static_cast<_Float16*>(dq), Sq, Sk, BH, nqt,
+                     scale);
+  rc = launched("fa_bwd dQ launch");
+  if (rc != FA_OK) return rc;
   hipLaunchKernelGGL(kv_kern, dim3((unsigned)kv_grid), dim3(64 * NW), kv_dyn, stream, Q, K, V, dO, l2, dvec,
                      static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), Sq, Sk, BH, (int)(kv_grid / BH), scale);
-  rc = launched("fa_bwd dK/dV launch");
-  if (rc != FA_OK) return rc;
-  hipLaunchKernelGGL(q_kern, dim3((unsigned)q_grid), dim3(64 * NW), q_dyn, stream, Q, K, V, dO, l2, dvec,
-                     static_cast<_Float16*>(dq), Sq, Sk, BH, nqt, scale);
-  return launched("fa_bwd dQ launch");
+  return launched("fa_bwd dK/dV launch");
 }
 
 std::atomic<int> g_cu_count[64];

@@ -7,9 +7,15 @@
 // forms dS = P o (dP - D) with dP = dO V^T, never storing P.  Then
 //   dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
 //
-// Three kernels, no atomics:
-//   bwd_dot_kernel    D_i = dO_i . O_i (fp32), one row per 16 lanes, and the
-//                     LSE in log2 units.
+// Two kernels, no atomics, the dQ kernel first:
+//   bwd_dq_kernel     one workgroup per (slice, 32*NW queries); each
+//                     wavefront owns 32 queries (Q and dO rows in registers)
+//                     and streams 64-key tiles of K and V through LDS:
+//                     S^T = K Q^T and dP^T = V dO^T put one query in each
+//                     lane, and dQ^T += K^T dS^T reads K transposed, like the
+//                     forward reads V.  It forms D_i = dO_i . O_i (fp32) from
+//                     the dO row it holds and writes D and the LSE in log2
+//                     units for the next kernel.
 //   bwd_dkdv_kernel   one workgroup per (slice, 32*NW keys); each wavefront
 //                     owns 32 keys (K and V rows in registers) and streams
 //                     32-query tiles of Q, dO, LSE and D through LDS:
@@ -19,12 +25,6 @@
 //                     transposed from LDS in the matching (permuted) query
 //                     order -- the forward's P V trick with queries and keys
 //                     exchanged.
-//   bwd_dq_kernel     one workgroup per (slice, 32*NW queries); each
-//                     wavefront owns 32 queries (Q and dO rows in registers)
-//                     and streams 64-key tiles of K and V through LDS:
-//                     S^T = K Q^T and dP^T = V dO^T put one query in each
-//                     lane, and dQ^T += K^T dS^T reads K transposed, like the
-//                     forward reads V.
 // Q/dO tiles (dkdv) and K tiles (dq) are read both row-wise and transposed,
 // so they use bswz, an XOR swizzle conflict-free for both reads.  Tiles go
 // HBM -> LDS with 16-byte direct copies one tile ahead of their use.
@@ -70,36 +70,6 @@ __host__ __device__ __forceinline__ void bswz_inv(int line, int slot, int& r, in
   } else {
     r = line * 4 + slot / 4;
     c = (slot % 4) ^ (line & 3);
-  }
-}
-
-// ---------------------------------------------------------------- D = dO . O
-
-template <int D>
-__global__ void __launch_bounds__(256)
-bwd_dot_kernel(const _Float16* __restrict__ O, const _Float16* __restrict__ dO, const float* __restrict__ LSE,
-               float* __restrict__ Dv, float* __restrict__ L2, int64_t rows) {
-  constexpr int LPR = (D / 8 < 16) ? D / 8 : 16;  // lanes per row
-  constexpr int CPL = (D / 8) / LPR;              // 16-byte chunks per lane
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / LPR;
-  const int dl = (int)(t % LPR);
-  float acc = 0.f;
-  if (row < rows) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const size_t off = (size_t)row * D + (dl + c * LPR) * 8;
-      const h8 a = as_h8(*reinterpret_cast<const u32x4*>(O + off));
-      const h8 b = as_h8(*reinterpret_cast<const u32x4*>(dO + off));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
-    }
-  }
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && dl == 0) {
-    Dv[row] = acc;
-    L2[row] = LSE[row] * kLog2e;  // the LSE in log2 units, for exp2
   }
 }
 
@@ -378,8 +348,9 @@ constexpr int dq_lds_bytes() {
 template <int D, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW, bwd_wg_per_cu<D>())
 bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, const _Float16* __restrict__ V,
-              const _Float16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
-              _Float16* __restrict__ dQ, int Sq, int Sk, int BH, int nqt, float scale) {
+              const _Float16* __restrict__ O, const _Float16* __restrict__ dO, const float* __restrict__ LSE,
+              float* __restrict__ L2, float* __restrict__ Dv, _Float16* __restrict__ dQ, int Sq, int Sk, int BH,
+              int nqt, float scale) {
   using C = BwdCfg<D, NW>;
   using L = DqLds<D>;
   constexpr int BN = L::BN;
@@ -405,16 +376,28 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
   const u32x4 rv = rsrc_words(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
 
   // Q and dO rows of this lane's query as the B operands of S^T = K Q^T and
-  // dP^T = V dO^T; its LSE (log2 units) and D.
+  // dP^T = V dO^T (this lane's half of each 16-wide step), its LSE in log2
+  // units and D = dO . O: this lane's half of the dot product, then the
+  // other half's from lane ^ 32.  Both go to L2 / Dv for the dK/dV kernel.
+  const auto ro = make_rsrc(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   h8 qreg[C::KS], doreg[C::KS];
+  float dhalf = 0.f;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    qreg[ks] = as_h8(buf_load16(rq, ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u));
-    doreg[ks] = as_h8(buf_load16(rdo, ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u));
+    const uint32_t off = ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u;
+    qreg[ks] = as_h8(buf_load16(rq, off));
+    doreg[ks] = as_h8(buf_load16(rdo, off));
+    const h8 o8 = as_h8(buf_load16(ro, off));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dhalf = __builtin_fmaf((float)o8[e], (float)doreg[ks][e], dhalf);
   }
   const bool qvalid = qi < Sq;
-  const float lse2 = qvalid ? L2[(size_t)bh * Sq + qi] : __builtin_huge_valf();
-  const float dval = qvalid ? Dv[(size_t)bh * Sq + qi] : 0.f;
+  const float dval = qvalid ? xhalf_sum(dhalf) : 0.f;
+  const float lse2 = qvalid ? LSE[(size_t)bh * Sq + qi] * kLog2e : __builtin_huge_valf();
+  if (qvalid && hh == 0) {
+    L2[(size_t)bh * Sq + qi] = lse2;
+    Dv[(size_t)bh * Sq + qi] = dval;
+  }
 
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + 32 * NW, Sk) + BN - 1) / BN) : nkt_all;
