@@ -148,10 +148,10 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
  * caller-owned device memory, 16-byte aligned (lse 4-byte); outputs must not
  * overlap inputs.  A per-row workspace (D and the LSE in log2 units,
  * fa_bwd_workspace_bytes) comes from the same per-device pool as
- * fa_decode_splitkv.  Three kernels run on `stream`: D_i, then dK and dV,
- * then dQ (the dK/dV and the dQ kernel each form S, P, dP and dS of their
- * tiles, so no partial sums cross workgroups and the result is bitwise
- * repeatable).  Supports D in {32, 64, 128, 256} (other D:
+ * fa_decode_splitkv.  Two kernels run on `stream`: dQ, which also forms D_i
+ * and the log2 LSE of every query row into the workspace, then dK and dV
+ * (each kernel forms S, P, dP and dS of its own tiles, so no partial sums
+ * cross workgroups and the result is bitwise repeatable).  Supports D in {32, 64, 128, 256} (other D:
  * FA_ERR_UNSUPPORTED); other errors as fa_fwd.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -295,6 +295,8 @@ int fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void*
  * count), and a sequence with no present key gets o = 0 and lse = -inf.
  * num_splits <= 0 picks fa_decode_auto_splits(B, H, max_blocks *
  * block_size, CUs); otherwise 1 <= num_splits <= max_blocks * block_size.
+ * At equal num_splits the result is bit-identical to fa_decode_splitkv on
+ * the same keys held contiguously (the keys are visited in the same order).
  * Workspace, pool and stream behaviour as fa_decode_splitkv.  Returns
  * FA_ERR_INVALID_ARG for null / misaligned pointers or bad sizes,
  * FA_ERR_UNSUPPORTED for D not in {32, 64, 128, 256}.
