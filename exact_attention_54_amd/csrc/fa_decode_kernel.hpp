@@ -46,7 +46,8 @@ struct DecCfg {
 // step, starting at a wave-uniform key `base`); a loader fills kr / vr with
 // the 16-byte chunks of this lane's keys base + u * SLOTS + slot whose
 // present[u] is set, clears present[u] for keys it finds absent, and leaves
-// zeros elsewhere.
+// zeros elsewhere.  start(base) is called once with the wavefront's first
+// base, before the first group.
 
 // Contiguous rows: key j of the slice is row j of k / v.
 template <int D, int T>
@@ -85,7 +86,7 @@ struct PagedLaneRows {
   const _Float16* __restrict__ k;
   const _Float16* __restrict__ v;
   const int* tbl;
-  int blk0, end, num_blocks, H, h, lbs, slot, dl;
+  int blk0, end, num_blocks, H, h, lbs, slot, dl;  // end: unused (the paged forms share one initializer)
   __device__ __forceinline__ void start(int) {}
   __device__ __forceinline__ void operator()(int base, bool (&present)[C::U], u32x4 (&kr)[C::U][C::CPL],
                                              u32x4 (&vr)[C::U][C::CPL]) const {
