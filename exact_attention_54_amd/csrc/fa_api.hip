@@ -317,6 +317,26 @@ int launch_fwd_kernel(unsigned grid, hipStream_t stream, const char* what, Args.
   return launched(what);
 }
 
+// The parts merge (fwd_merge_kernel) instantiated for the smallest bound
+// on the parts that holds ns (the parts planner cuts at most 8, Split-D at
+// most 16).
+template <int D>
+int launch_fwd_merge(const float* ws_o, const float* ws_lse, void* o, float* lse, int Sq, int BM, int ts,
+                     int nsplit, int ns, int64_t rows, hipStream_t stream, const char* what) {
+  if (ns < 1 || ns > 16) return fail(FA_ERR_INVALID_ARG, "%s: %d key parts (at most 16)", what, ns);
+  auto go = [&](auto bound) {
+    constexpr int NP = decltype(bound)::value;
+    constexpr int R = fa::MergeCfg<D, NP>::ROWS;
+    hipLaunchKernelGGL((fa::fwd_merge_kernel<D, NP>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
+                       ws_o, ws_lse, static_cast<_Float16*>(o), lse, Sq, BM, ts, nsplit, ns, (int)rows);
+    return launched(what);
+  };
+  if (ns <= 2) return go(std::integral_constant<int, 2>{});
+  if (ns <= 4) return go(std::integral_constant<int, 4>{});
+  if (ns <= 8) return go(std::integral_constant<int, 8>{});
+  return go(std::integral_constant<int, 16>{});
+}
+
 template <int D, int BN, int NW, bool CAUSAL>
 int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Sq, int Sk,
                      float scale, hipStream_t stream, const SplitPlan& pl, void* ws) {
@@ -357,11 +377,8 @@ int launch_fwd_split(const void* q, const void* k, const void* v, void* o, float
         static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, Sq, Sk,
         BH, nqt, scale * fa::kLog2e, fa::VarlenArgs{}, ksp);
     if (rc != FA_OK) return rc;
-    constexpr int R = fa::MergeCfg<D>::ROWS;
-    hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream,
-                       ksp.ws_o, ksp.ws_lse, static_cast<_Float16*>(o), lse, Sq, Cfg::BM, pl.ts, nsplit, pl.ns,
-                       (int)rows);
-    return launched("fa_fwd key-split merge launch");
+    return launch_fwd_merge<D>(ksp.ws_o, ksp.ws_lse, o, lse, Sq, Cfg::BM, pl.ts, nsplit, pl.ns, rows, stream,
+                               "fa_fwd key-split merge launch");
   }
 }
 
@@ -456,10 +473,7 @@ int launch_fwd_splitd(const void* q, const void* k, const void* v, void* o, floa
   // tile of Sq rows per slice in the merge kernel's terms
   const int64_t rows = (int64_t)BH * Sq;
   if (rows > kMaxGrid) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  constexpr int R = fa::MergeCfg<D>::ROWS;
-  hipLaunchKernelGGL((fa::fwd_merge_kernel<D>), dim3((unsigned)((rows + R - 1) / R)), dim3(256), 0, stream, ws_o,
-                     ws_lse, static_cast<_Float16*>(o), lse, Sq, Sq, 0, 1, ns, (int)rows);
-  return launched("fa_fwd Split-D merge launch");
+  return launch_fwd_merge<D>(ws_o, ws_lse, o, lse, Sq, Sq, 0, 1, ns, rows, stream, "fa_fwd Split-D merge launch");
 }
 
 // Workgroup size of the single-partition decode (its in-LDS merge writes

@@ -774,25 +774,28 @@ fwd_split_merge_kernel(KeySplit ksp, _Float16* __restrict__ O, float* __restrict
   }
 }
 
-// Merge of the key parts of the Split-D forward: for each query row,
-// lse = ln sum_p e^(lse_p) and O = sum_p e^(lse_p - lse) O_p, the log-sum-exp
-// combination of partial softmax results ("Adaptive High-Performance
-// Attention Kernels in CUDA", Split-K / Flash-Decoding, phase two).  D/4
-// threads per row, 4 consecutive d each (16-byte loads); 256 / (D/4) rows
-// per workgroup.  Row = (slice, tile - ts, row in tile), written to
-// O[slice, (ts + tile) * BM + row] and LSE at the same position.
-template <int D>
+// Merge of the key parts of a split forward (the parts of the D <= 128
+// key split and of the Split-D forward): for each query row, lse = ln sum_p
+// e^(lse_p) and O = sum_p e^(lse_p - lse) O_p, the log-sum-exp combination
+// of partial softmax results ("Adaptive High-Performance Attention Kernels
+// in CUDA", Split-K / Flash-Decoding, phase two).  D/4 threads per row, 4
+// consecutive d each (16-byte loads), 256 / (D/4) rows per workgroup; all
+// loads of a thread's parts (up to NP, an instantiation per bound) are
+// issued before any is used, so a row waits for one memory round trip.
+// Row = (slice, tile - ts, row in tile), written to O[slice, (ts + tile) *
+// BM + row] and LSE at the same position.
+template <int D, int NP>
 struct MergeCfg {
   static constexpr int TPR = D / 4;         // threads per row
   static constexpr int ROWS = 256 / TPR;    // rows per workgroup
-  static_assert(D % 4 == 0 && TPR <= 256 && 256 % TPR == 0, "merge geometry");
+  static_assert(D % 4 == 0 && TPR <= 256 && 256 % TPR == 0 && NP >= 1 && NP <= 16, "merge geometry");
 };
 
-template <int D>
+template <int D, int NP>
 __global__ void __launch_bounds__(256)
 fwd_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, _Float16* __restrict__ O,
                  float* __restrict__ LSE, int Sq, int BM, int ts, int nsplit, int ns, int rows) {
-  using M = MergeCfg<D>;
+  using M = MergeCfg<D, NP>;
   const int row = (int)blockIdx.x * M::ROWS + (int)threadIdx.x / M::TPR;
   const int d0 = 4 * ((int)threadIdx.x % M::TPR);
   if (row >= rows) return;
@@ -801,23 +804,36 @@ fwd_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ls
   const int bh = row / (BM * nsplit);
   const int q = (ts + tl) * BM + r;
   if (q >= Sq) return;
-  const float* lp = ws_lse + (size_t)row * ns;
-  const float* op = ws_o + (size_t)row * ns * D + d0;
   const size_t out = (size_t)bh * Sq + q;
+  float lp[NP];
+  f32x4 xp[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    lp[j] = kNegInf;
+    xp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j < ns) {
+      lp[j] = ws_lse[(size_t)row * ns + j];
+      xp[j] = *reinterpret_cast<const f32x4*>(ws_o + ((size_t)row * ns + j) * D + d0);
+    }
+  }
   float mx = kNegInf;
-  for (int p = 0; p < ns; ++p) mx = fmaxf(mx, lp[p]);
+#pragma unroll
+  for (int j = 0; j < NP; ++j)
+    if (j < ns) mx = fmaxf(mx, lp[j]);
   h4 res;
   if (mx == kNegInf) {  // no key in any part: O = 0, LSE = -inf
     res = h4{0, 0, 0, 0};
   } else {
     float den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < ns; ++p) {
-      const float wgt = exp2_fast((lp[p] - mx) * kLog2e);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(op + (size_t)p * D);
-      den += wgt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] += wgt * x[e];
+    for (int j = 0; j < NP; ++j) {
+      if (j < ns) {
+        const float wgt = exp2_fast((lp[j] - mx) * kLog2e);
+        den += wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] += wgt * xp[j][e];
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) res[e] = (_Float16)(num[e] / den);
