@@ -456,9 +456,28 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   const int d0 = 4 * ((int)threadIdx.x % M::TPR);
   const float* lp = ws_lse + (size_t)bh * ns;
   const float* op = ws_o + (size_t)bh * ns * D + d0;
+  // the lse and partial O of the group's first NPG partitions are loaded
+  // together, before the maximum is known (one memory round trip); any
+  // further partitions are read in a loop below
+  constexpr int NPG = 4;
+  float lv[NPG];
+  f32x4 xv[NPG];
+#pragma unroll
+  for (int i = 0; i < NPG; ++i) {
+    const int s = g + i * M::G;
+    lv[i] = kNegInf;
+    xv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s < ns) {
+      lv[i] = lp[s];
+      xv[i] = *reinterpret_cast<const f32x4*>(op + (size_t)s * D);
+    }
+  }
   // lse max over the partitions: per group, then across the groups
   float mx = kNegInf;
-  for (int s = g; s < ns; s += M::G) mx = fmaxf(mx, lp[s]);
+#pragma unroll
+  for (int i = 0; i < NPG; ++i)
+    if (g + i * M::G < ns) mx = fmaxf(mx, lv[i]);
+  for (int s = g + NPG * M::G; s < ns; s += M::G) mx = fmaxf(mx, lp[s]);
   if (d0 == 0) s_max[g] = mx;
   __syncthreads();
   mx = s_max[0];
@@ -473,7 +492,16 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   }
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s = g; s < ns; s += M::G) {
+#pragma unroll
+  for (int i = 0; i < NPG; ++i) {
+    if (g + i * M::G < ns) {
+      const float wgt = exp2_fast((lv[i] - mx) * kLog2e);
+      den += wgt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += wgt * xv[i][e];
+    }
+  }
+  for (int s = g + NPG * M::G; s < ns; s += M::G) {
     const float wgt = exp2_fast((lp[s] - mx) * kLog2e);
     const f32x4 x = *reinterpret_cast<const f32x4*>(op + (size_t)s * D);
     den += wgt;
