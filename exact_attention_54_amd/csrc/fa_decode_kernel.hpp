@@ -168,7 +168,7 @@ struct PagedGroupRows {
 // or absent in the loader's view score -inf.  Contiguous and paged rows
 // walk the keys in the same order, so their results agree bit for bit.
 template <int D, int T, class Load>
-__device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::CPL][8], int a0, int kb, int ke,
+__device__ __forceinline__ void decode_accumulate(const h8 (&qh)[DecCfg<D>::CPL], int a0, int kb, int ke,
                                                   Load& load, int w, int slot, float c2, float& m_run,
                                                   float& l_run, float (&acc)[DecCfg<D>::CPL][8]) {
   using C = DecCfg<D, T>;
@@ -190,7 +190,7 @@ __device__ __forceinline__ void decode_accumulate(const float (&qf)[DecCfg<D>::C
       for (int c = 0; c < C::CPL; ++c) {
         const h8 kh = as_h8(kr[u][c]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qf[c][e], (float)kh[e], part);
+        for (int e = 0; e < 8; e += 2) part = dot2(h2{kh[e], kh[e + 1]}, h2{qh[c][e], qh[c][e + 1]}, part);
       }
 #pragma unroll
       for (int off = 1; off < C::LPK; off <<= 1) part += __shfl_xor(part, off);
@@ -313,13 +313,11 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
   }
 
   const _Float16* qp = Q + (size_t)bh * D;
-  float qf[C::CPL][8];
+  // q stays fp16: the scores are fp32 sums of fp16 products (v_dot2), so no
+  // conversion waits for q before the first K / V loads are issued
+  h8 qh[C::CPL];
 #pragma unroll
-  for (int c = 0; c < C::CPL; ++c) {
-    const h8 t = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[c][e] = (float)t[e];
-  }
+  for (int c = 0; c < C::CPL; ++c) qh[c] = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
 
   float m_run = kNegInf, l_run = 0.f;
   float acc[C::CPL][8];
@@ -329,7 +327,7 @@ decode_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
 
   ContigRows<D, T> rows{K + (size_t)bh * Sk * D, V + (size_t)bh * Sk * D, slot, dl};
-  decode_accumulate<D, T>(qf, k0 & ~(C::KEYS_PER_WAVE_ITER - 1), k0, k1, rows, w, slot, c2, m_run, l_run, acc);
+  decode_accumulate<D, T>(qh, k0 & ~(C::KEYS_PER_WAVE_ITER - 1), k0, k1, rows, w, slot, c2, m_run, l_run, acc);
   decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
 
@@ -393,13 +391,11 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
   }
 
   const _Float16* qp = Q + (size_t)bh * D;
-  float qf[C::CPL][8];
+  // q stays fp16: the scores are fp32 sums of fp16 products (v_dot2), so no
+  // conversion waits for q before the first K / V loads are issued
+  h8 qh[C::CPL];
 #pragma unroll
-  for (int c = 0; c < C::CPL; ++c) {
-    const h8 t = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[c][e] = (float)t[e];
-  }
+  for (int c = 0; c < C::CPL; ++c) qh[c] = as_h8(*reinterpret_cast<const u32x4*>(qp + (dl + c * C::LPK) * 8));
 
   float m_run = kNegInf, l_run = 0.f;
   float acc[C::CPL][8];
@@ -424,7 +420,7 @@ decode_paged_partial_kernel(const _Float16* __restrict__ Q, const _Float16* __re
     __syncthreads();
     using Rows = std::conditional_t<GROUP, PagedGroupRows<D, T>, PagedLaneRows<D, T>>;
     Rows rows{Kc, Vc, s_tbl, blk0, seg_end, num_blocks, H, h, lbs, slot, dl};
-    decode_accumulate<D, T>(qf, seg, max(seg, k0), seg_end, rows, w, slot, c2, m_run, l_run, acc);
+    decode_accumulate<D, T>(qh, seg, max(seg, k0), seg_end, rows, w, slot, c2, m_run, l_run, acc);
   }
   decode_merge_slots<D, T, FINAL>(m_run, l_run, acc, tid, w, slot, dl, out_o, out_h, out_lse);
 }
