@@ -375,30 +375,6 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
   const u32x4 rk = rsrc_words(K + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
   const u32x4 rv = rsrc_words(V + (size_t)bh * Sk * D, (uint32_t)Sk * D * 2);
 
-  // Q and dO rows of this lane's query as the B operands of S^T = K Q^T and
-  // dP^T = V dO^T (this lane's half of each 16-wide step), its LSE in log2
-  // units and D = dO . O: this lane's half of the dot product, then the
-  // other half's from lane ^ 32.  Both go to L2 / Dv for the dK/dV kernel.
-  const auto ro = make_rsrc(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
-  h8 qreg[C::KS], doreg[C::KS];
-  float dhalf = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    const uint32_t off = ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u;
-    qreg[ks] = as_h8(buf_load16(rq, off));
-    doreg[ks] = as_h8(buf_load16(rdo, off));
-    const h8 o8 = as_h8(buf_load16(ro, off));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dhalf = __builtin_fmaf((float)o8[e], (float)doreg[ks][e], dhalf);
-  }
-  const bool qvalid = qi < Sq;
-  const float dval = qvalid ? xhalf_sum(dhalf) : 0.f;
-  const float lse2 = qvalid ? LSE[(size_t)bh * Sq + qi] * kLog2e : __builtin_huge_valf();
-  if (qvalid && hh == 0) {
-    L2[(size_t)bh * Sq + qi] = lse2;
-    Dv[(size_t)bh * Sq + qi] = dval;
-  }
-
   const int nkt_all = (Sk + BN - 1) / BN;
   const int nkt = CAUSAL ? min(nkt_all, (min(q0 + 32 * NW, Sk) + BN - 1) / BN) : nkt_all;
   const int jlast = (qw >= Sq) ? -1 : (CAUSAL ? min(nkt - 1, (qw + 31) / BN) : nkt - 1);
@@ -430,13 +406,45 @@ bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K, co
     }
   };
 
+  // Q and dO rows of this lane's query as the B operands of S^T = K Q^T and
+  // dP^T = V dO^T (this lane's half of each 16-wide step), its LSE in log2
+  // units and D = dO . O: this lane's half of the dot product, then the
+  // other half's from lane ^ 32.  Both go to L2 / Dv for the dK/dV kernel.
+  // The row loads and the first K / V tile copy are all issued before any
+  // of them is waited for (one memory round trip before the loop).
+  const auto ro = make_rsrc(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  const bool qvalid = qi < Sq;
+  // read unconditionally (rows past Sq read row Sq - 1 and are not used), so
+  // no branch around the load makes its use wait at once
+  const float lse_in = LSE[(size_t)bh * Sq + min(qi, Sq - 1)];
+  h8 qreg[C::KS], doreg[C::KS], oreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const uint32_t off = ((uint32_t)qi * D + 16 * ks + 8 * hh) * 2u;
+    qreg[ks] = as_h8(buf_load16(rq, off));
+    doreg[ks] = as_h8(buf_load16(rdo, off));
+    oreg[ks] = as_h8(buf_load16(ro, off));
+  }
+  if (nkt > 0) load_stage(0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // the uses below stay after the copies' issue
+  float dhalf = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dhalf = __builtin_fmaf((float)oreg[ks][e], (float)doreg[ks][e], dhalf);
+  const float dval = qvalid ? xhalf_sum(dhalf) : 0.f;
+  const float lse2 = qvalid ? lse_in * kLog2e : __builtin_huge_valf();
+  if (qvalid && hh == 0) {
+    L2[(size_t)bh * Sq + qi] = lse2;
+    Dv[(size_t)bh * Sq + qi] = dval;
+  }
+
   f32x16 dqt[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqt[db][j] = 0.f;
 
-  if (nkt > 0) load_stage(0, 0);
   wait_vmem_all();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
