@@ -609,13 +609,13 @@ def main():
 
     src_hash = kernel_source_hash()
     roof_pre = {
-        "kernel": "fwd_kernel<128,64,causal>",
+        "kernel": "fwd_kernel<128,32,causal>",
         "bound": "mfma",
         "achieved": round(tflops, 3),
         "peak": PEAK_FP16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-        "traffic": measured_traffic(["fwd_kernel<128,64,causal>"], src_hash),
+        "traffic": measured_traffic(["fwd_kernel<128,32,causal>"], src_hash),
     }
     # one partition: a single kernel splits the keys over the 16 wavefronts
     # of a 1024-thread workgroup and merges them in LDS
